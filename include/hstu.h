@@ -1,0 +1,150 @@
+/*
+ * hstu.h -- C ABI of the MI355X (gfx950) fused HSTU attention forward.
+ *
+ * Operation (RecOps Running Case Documentation, HSTU_V1 forward operator
+ * page: the feature table's attention row, the operator introduction and the
+ * inputs/outputs table). For every query head h and every query token i of
+ * sequence b, with kv head hk = floor(h * num_heads_kv / num_heads_q):
+ *
+ *   O[i, h, :] = out_scale * sum_{j visible to i}
+ *                  silu(alpha * (Q[i,h,:] . K[j,hk,:] + rab[b,h,i,j])) * V[j,hk,:]
+ *
+ * with silu(x) = x / (1 + exp(-x)). There is no softmax and no running max.
+ * The page leaves three placements open; this library reads them as:
+ * rab is added before alpha scales, the page's silu_scale is out_scale and
+ * multiplies after SiLU, and P = silu(...) is rounded to the input dtype
+ * before the product with V (fp32 accumulation throughout).
+ *
+ * Masks (the page's mask_type codes): HSTU_MASK_CAUSAL (0) is the built-in
+ * lower-triangular mask with context and targets; HSTU_MASK_NONE (2) is the
+ * bidirectional case. Codes 1 (upper triangular, unsupported by the page
+ * itself) and 3 (user mask tensor) return HSTU_ERR_UNSUPPORTED.
+ * For HSTU_MASK_CAUSAL, per sequence of length L with nc = num_context[b],
+ * nt = num_targets[b] (0 when the array is NULL) and g = target_group_size:
+ * clamp nt to [0, L], H = L - nt, clamp nc to [0, H]. Key j < H is visible to
+ * query i iff j <= i, or both i and j are context tokens (< nc). Key j >= H
+ * (a target) is visible iff j <= i when g == 0; when g >= 1 only if i is a
+ * target of the same group of g consecutive targets and j <= i.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE memory owned by the caller. The library
+ *    never allocates, frees, retains or reads them on the host, and never
+ *    synchronises: work is enqueued on `stream` and the call returns.
+ *  - Tensors are contiguous, row-major, 16-byte aligned.
+ *  - Integer side inputs are int32 device arrays.
+ *  - `workspace` is caller-allocated device memory of at least the size the
+ *    matching *_workspace_size call returns; its contents need no
+ *    initialisation and are scratch after the call. Calls that share one
+ *    workspace must be ordered on one stream.
+ *  - Validity of device arrays (offsets non-decreasing from 0, every length
+ *    <= max_seq_len, page ids in range) is the caller's duty, as the page
+ *    says for seq_offsets; it is not checked.
+ *  - Return codes only; nothing is thrown across the ABI.
+ *  - If batch, num_heads_q or head_dim is 0 the input is empty: the call
+ *    returns HSTU_OK and launches nothing (the page's note on empty inputs).
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = 1, /* bad size, null required pointer, misaligned pointer, bad combination */
+  HSTU_ERR_UNSUPPORTED = 2, /* valid per the page but not built here (mask codes 1/3, head_dim, page_size) */
+  HSTU_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
+  HSTU_ERR_HIP = 4          /* a HIP launch failed; the HIP error is left for hipGetLastError */
+} hstu_status_t;
+
+typedef enum { HSTU_F32 = 0, HSTU_F16 = 1, HSTU_BF16 = 2 } hstu_dtype_t;
+
+typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2 } hstu_mask_t;
+
+/* Supported sizes: head_dim in {32, 64, 128, 256} for f16/bf16 and
+ * {32, 64, 128} for f32 (the page allows multiples of 16 up to 512);
+ * num_heads_q % num_heads_kv == 0 (the page's GQA rule); page_size in
+ * {32, 64, 128, 256}; max_seq_len in [1, 20480]. */
+
+/*
+ * Workspace bytes hstu_fwd needs for these sizes (the work list of the tile
+ * scheduler and the split-K partial sums). Returns 0 for invalid sizes.
+ */
+size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
+                               int32_t head_dim, hstu_dtype_t dtype);
+
+/*
+ * Jagged forward (the page's "jagged" layout, seq_offsets_q == seq_offsets_k).
+ *  q           [T, num_heads_q,  head_dim]  dtype   (T = seq_offsets[batch])
+ *  k, v        [T, num_heads_kv, head_dim]  dtype
+ *  rab         [batch, num_heads_q, max_seq_len, max_seq_len] dtype, or NULL.
+ *              Indexed by positions local to the sequence; only visible
+ *              (i, j) inside the sequence are read.
+ *  out         [T, num_heads_q, head_dim]   dtype (written for every token)
+ *  seq_offsets [batch + 1] int32, non-decreasing, seq_offsets[0] == 0.
+ *  num_context, num_targets [batch] int32, or NULL (= all zero). Must be
+ *              NULL with HSTU_MASK_NONE.
+ *  target_group_size >= 0 (0 = no target mask).
+ *  alpha       scale applied to (Q.K^T + rab) before SiLU.
+ *  out_scale   scale applied after SiLU (the page's silu_scale; its default
+ *              is 1/max_seq_len, applied by the Python binding).
+ * Errors: HSTU_ERR_INVALID_ARG for negative sizes, num_heads_q not a
+ * multiple of num_heads_kv, null q/k/v/out/seq_offsets, pointers not 16-byte
+ * aligned, num_context/num_targets with HSTU_MASK_NONE, target_group_size <
+ * 0; HSTU_ERR_UNSUPPORTED for other mask codes, head_dim or dtype;
+ * HSTU_ERR_WORKSPACE if workspace_bytes is too small; HSTU_ERR_HIP if a
+ * launch fails.
+ */
+hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* rab, void* out,
+                       const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
+                       int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
+                       int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
+                       float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       void* stream /* hipStream_t */);
+
+/*
+ * Workspace bytes hstu_fwd_paged needs. max_seq_len bounds history + new
+ * tokens of every request. Returns 0 for invalid sizes.
+ */
+size_t hstu_fwd_paged_workspace_size(int32_t batch, int32_t page_size, int32_t max_seq_len, int32_t num_heads_q,
+                                     int32_t num_heads_kv, int32_t head_dim, hstu_dtype_t dtype);
+
+/*
+ * Paged-KV forward (the page's Page feature row and its kv_cache,
+ * page_offsets, page_ids and last_page_len inputs). The cache holds each
+ * request's history; the new tokens bring their own K/V.
+ *  q              [Tq, num_heads_q, head_dim]   new tokens' queries (Tq = seq_offsets_q[batch])
+ *  k_new, v_new   [Tq, num_heads_kv, head_dim]  new tokens' keys/values
+ *  out            [Tq, num_heads_q, head_dim]
+ *  seq_offsets_q  [batch + 1] int32: new tokens per request.
+ *  kv_cache       [num_pages, 2, page_size, num_heads_kv, head_dim]: [p,0] = K, [p,1] = V.
+ *  page_offsets   [batch + 1] int32; page_ids [page_offsets[batch]] int32;
+ *  last_page_len  [batch] int32 in [1, page_size]. Request b's history has
+ *                 (n_pages - 1) * page_size + last_page_len[b] tokens (0 if
+ *                 it owns no page).
+ * Query t of request b sits at absolute position history_len + t of a
+ * sequence of history_len + Tq_b tokens; the mask (num_context, num_targets,
+ * target_group_size) is applied on those absolute positions. No rab.
+ * Errors as hstu_fwd, plus HSTU_ERR_UNSUPPORTED for page_size outside
+ * {32, 64, 128, 256}.
+ */
+hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new, void* out,
+                             const int32_t* seq_offsets_q, const void* kv_cache, const int32_t* page_offsets,
+                             const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
+                             const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
+                             int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
+                             int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
+                             void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/* Static description of a status code. Never NULL. */
+const char* hstu_status_string(hstu_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */
