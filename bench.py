@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused HSTU attention forward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input already
+resident in HBM: the tile scheduler (hstu_*_plan) and the fused forward
+kernel (hstu_*_run), both through the C ABI. Prints ONE JSON line:
+effective TFLOP/s = 4 * head_dim * (visible query/key pairs summed over
+query heads) / wall time per step, with the dominant kernel's roofline
+(achieved vs MI355X's dense MFMA peak, per-launch time from HIP events on
+the launch stream) and the float64 CPU oracle timed on the host as a
+baseline.
+
+Default workload: bf16 MHA jagged causal, batch 8, lengths ~ U{256..1024},
+4 heads, head_dim 128.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+ELEM = {"bf16": 2, "f16": 2, "f32": 4}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bf16_mha_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload (extra lines for analysis)")
+    return ap.parse_args()
+
+
+def build_step(name, dev):
+    import torch
+    import hstu_jagged_attention_amd as hj
+    from hstu_jagged_attention_amd import metrics
+    from hstu_jagged_attention_amd import workloads as wl
+    c = wl.WORKLOADS[name]()
+    if name == "bf16_paged_target":
+        prep = hj.prepare_fwd_paged(c.q.to(dev), c.k_new.to(dev), c.v_new.to(dev), c.kv_cache.to(dev),
+                                    torch.as_tensor(c.seq_offsets_q), torch.as_tensor(c.page_offsets),
+                                    torch.as_tensor(c.page_ids), torch.as_tensor(c.last_page_len),
+                                    num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                                    mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                                    out_scale=c.out_scale)
+        pairs = metrics.pairs_paged(c.history_lengths, c.new_lengths, c.num_context, c.num_targets,
+                                    c.target_group_size, c.mask_type)
+        Tq = int(c.seq_offsets_q[-1])
+        alg_bytes = metrics.algorithmic_bytes_paged(Tq, int(c.history_lengths.sum()), c.num_heads_q, c.num_heads_kv,
+                                                    c.head_dim, ELEM[c.dtype])
+        desc = dict(batch=c.batch, history="U{512..4096}", new_tokens="U{1..64}", page_size=c.page_size,
+                    total_new_tokens=Tq, total_history_tokens=int(c.history_lengths.sum()))
+    else:
+        prep = hj.prepare_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets),
+                              rab=None if c.rab is None else c.rab.to(dev), num_context=c.num_context,
+                              num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
+                              target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
+        pairs = metrics.pairs_jagged(c.seq_offsets, c.num_context, c.num_targets, c.target_group_size, c.mask_type)
+        T = int(c.seq_offsets[-1])
+        alg_bytes = metrics.algorithmic_bytes_jagged(T, c.num_heads_q, c.num_heads_kv, c.head_dim, ELEM[c.dtype],
+                                                     pairs if c.rab is not None else 0)
+        desc = dict(batch=c.batch, total_tokens=T, max_seq_len=c.max_seq_len, lengths_min=int(c.lengths.min()),
+                    lengths_max=int(c.lengths.max()))
+    flops = metrics.effective_flops(pairs, c.num_heads_q, c.head_dim)
+    desc.update(num_heads_q=c.num_heads_q, num_heads_kv=c.num_heads_kv, head_dim=c.head_dim,
+                mask="causal" if c.mask_type == 0 else "bidirectional", rab=bool(getattr(c, "rab", None) is not None),
+                visible_pairs_per_head=pairs)
+    return c, prep, flops, alg_bytes, desc
+
+
+def cpu_baseline(c, name, flops_full):
+    """The float64 oracle on the host cores over the same inputs (whole
+    workload when that is a few seconds of CPU work, else a row sample)."""
+    import numpy as np
+    import oracle
+    from hstu_jagged_attention_amd import metrics
+
+    def f64(t):
+        return t.double().numpy()
+
+    if name == "bf16_paged_target":
+        run = lambda: oracle.hstu_fwd_paged(f64(c.q), f64(c.k_new), f64(c.v_new), f64(c.kv_cache), c.seq_offsets_q,
+                                            c.page_offsets, c.page_ids, c.last_page_len, num_context=c.num_context,
+                                            num_targets=c.num_targets, mask_type=c.mask_type,
+                                            target_group_size=c.target_group_size, alpha=c.alpha,
+                                            out_scale=c.out_scale)
+        sample, fl = "whole workload", flops_full
+    elif name in ("bf16_mha_causal", "tiny_fp32_bidirectional"):
+        q, k, v = f64(c.q), f64(c.k), f64(c.v)
+        run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, num_context=c.num_context, num_targets=c.num_targets,
+                                      max_seq_len=c.max_seq_len, mask_type=c.mask_type,
+                                      target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
+        sample, fl = "whole workload", flops_full
+    else:
+        # Row sample: every 16th token of every sequence, all heads.
+        q, k, v = f64(c.q), f64(c.k), f64(c.v)
+        rows, pairs = [], 0
+        for b in range(c.batch):
+            s0, L = int(c.seq_offsets[b]), int(c.lengths[b])
+            nc = 0 if c.num_context is None else int(c.num_context[b])
+            nt = 0 if c.num_targets is None else int(c.num_targets[b])
+            per_row = metrics.visible_per_row(L, nc, nt, c.target_group_size, c.mask_type)
+            for i in range(0, L, 16):
+                rows += [(s0 + i, h) for h in range(c.num_heads_q)]
+                pairs += int(per_row[i]) * c.num_heads_q
+        rab = None if c.rab is None else f64(c.rab)
+        run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, num_context=c.num_context,
+                                      num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
+                                      target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale,
+                                      rows=rows)
+        sample, fl = "every 16th query row of every sequence, all heads", 4.0 * c.head_dim * pairs
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}; median of 3 runs, {t:.3f} s each"}
+
+
+def measure(name, args, dev):
+    import torch
+    c, prep, flops, alg_bytes, desc = build_step(name, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        prep.plan()
+        prep.run()
+    torch.cuda.synchronize(dev)
+    # Timed region: exactly K steps.
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        prep.plan()
+        prep.run()
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # Per-kernel launch durations with HIP events on the launch stream.
+    n_ev = max(args.steps, 10)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for e in ev:
+        e[0].record(stream)
+        prep.plan()
+        e[1].record(stream)
+        prep.run()
+        e[2].record(stream)
+    torch.cuda.synchronize(dev)
+    plan_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    run_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in ev)
+    run_ms_median = statistics.median(e[1].elapsed_time(e[2]) for e in ev)
+    achieved_tflops = flops / (run_ms * 1e-3) / 1e12
+    dtype = c.dtype
+    peak = PEAK_TFLOPS[dtype]
+    hbm_gbs = alg_bytes / (run_ms * 1e-3) / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved_tflops / peak, 4), "traffic": None,
+                "kernel": "fwd_kernel", "launch_ms_mean": round(run_ms, 5), "launch_ms_median": round(run_ms_median, 5),
+                "plan_kernel_ms_mean": round(plan_ms, 5), "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
+                "algorithmic_hbm_GBps": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    res = {"metric": "HSTU fwd effective TFLOP/s (unmasked pairs) + % of bf16 MFMA peak, 1 GPU",
+           "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": dtype, "data": "synthetic (seeded numpy draws, rounded to dtype)",
+           "config": dict(workload=name, **desc), "pct_of_mfma_peak": round(100 * value / peak, 2),
+           "roofline": roofline}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(c, name, flops)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
+              "path; see the sharding note in the design document)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import hstu_jagged_attention_amd as hj
+    hj.load_library()
+    dev = torch.device("cuda:0")
+    names = ["tiny_fp32_bidirectional", "bf16_mha_causal", "bf16_rab_target", "fp16_gqa_causal",
+             "bf16_paged_target"] if args.all else [args.workload]
+    for name in names:
+        print(f"[bench] {name}: building inputs", file=sys.stderr, flush=True)
+        res = measure(name, args, dev)
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

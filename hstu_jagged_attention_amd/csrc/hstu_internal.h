@@ -1,0 +1,57 @@
+// Internal launch interface between the C ABI (hstu_abi.cpp) and the gfx950
+// kernels (hstu_kernels.hip). Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hstu {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Everything one forward launch needs. Pointers are device memory.
+struct FwdArgs {
+  DType dtype;
+  bool causal;
+  bool paged;
+  const void* q;
+  const void* k;  // jagged: k; paged: k_new
+  const void* v;  // jagged: v; paged: v_new
+  const void* rab;
+  void* out;
+  const int32_t* seq_offsets;  // jagged: [B+1]; paged: new tokens per request [B+1]
+  const int32_t* num_context;
+  const int32_t* num_targets;
+  const void* kv_cache;
+  const int32_t* page_offsets;
+  const int32_t* page_ids;
+  const int32_t* last_page_len;
+  int32_t page_size;
+  int32_t batch;
+  int32_t max_seq_len;
+  int32_t num_heads_q;
+  int32_t num_heads_kv;
+  int32_t head_dim;
+  int32_t target_group_size;
+  float alpha;
+  float out_scale;
+  void* workspace;
+  size_t workspace_bytes;
+  hipStream_t stream;
+};
+
+// Bytes of workspace the launch needs (work list + queue counters).
+size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
+                           int32_t head_dim, DType dtype);
+
+// Enqueues the planner on args.stream: it writes the work list into the
+// workspace and zeroes the work-queue counters.
+hipError_t launch_plan(const FwdArgs& args);
+
+// Enqueues the forward kernel on args.stream; it consumes the work list the
+// planner left in the workspace (same sizes and mask inputs) and leaves the
+// queue counters at zero when it ends, so one plan serves many runs.
+hipError_t launch_run(const FwdArgs& args);
+
+}  // namespace hstu

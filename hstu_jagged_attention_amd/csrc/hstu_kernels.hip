@@ -1,0 +1,837 @@
+// gfx950 (MI355X, CDNA4) kernels of the fused HSTU attention forward.
+//
+// Operation (RecOps Running Case Documentation, HSTU_V1 forward operator:
+// feature table, operator introduction, inputs/outputs table): per query
+// head, O = out_scale * (M .* silu(alpha * (Q K^T + rab))) V over jagged
+// sequences, MHA or GQA, with the bidirectional mask or the causal mask
+// built from num_context / num_targets / target_group_size, and a paged
+// variant whose history K/V live in kv_cache pages. No softmax: partial sums
+// over key tiles add exactly, so no running max or rescale is kept.
+//
+// Two kernels per call, both on the caller's stream:
+//  1. plan_kernel: one workgroup turns seq_offsets (and the mask inputs)
+//     into the work list: one item per (sequence, query tile), costed by the
+//     number of key tiles that are not fully masked, counting-sorted longest
+//     first. It also zeroes the work-queue counter.
+//  2. fwd_kernel: persistent workgroups of 4 waves pop items from the queue
+//     in list order. A workgroup owns one item and a group of query heads
+//     that share one kv head (1 head x 128 rows for MHA, up to 4 heads x 32
+//     rows for GQA), so each K/V tile is staged through LDS once for all of
+//     them. Per key tile: S^T = K Q^T on MFMA (the accumulator then holds
+//     one query per lane and 16 keys per lane), the SiLU epilogue in
+//     registers, then O^T += V^T P^T on MFMA with P used straight from the
+//     S^T registers as the B operand. The key order inside a 32-key block is
+//     permuted (bits 2 and 3 swapped) when V^T is written to LDS, so both
+//     MFMA operands of the second product read 16 contiguous bytes per lane.
+//
+// MFMA lane layouts (checked on the device): v_mfma_f32_32x32x16_{bf16,f16}
+// takes A[m = lane%32][k = 8*(lane/32) + 0..7] and B[k = 8*(lane/32) + 0..7]
+// [n = lane%32] and returns C[m = 8*(r/4) + 4*(lane/32) + r%4][n = lane%32]
+// in register r; v_mfma_f32_32x32x2f32 takes one k per half-wave.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "hstu_internal.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kMaxBins = 1024;  // > max key tiles of one row (20480 / 32)
+constexpr int kPlanThreads = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef _Float16 f16x8_t __attribute__((__vector_size__(16)));
+typedef float f32x16_t __attribute__((__vector_size__(64)));
+typedef float f32x4_t __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4_t __attribute__((__vector_size__(16)));
+typedef uint32_t u32x2_t __attribute__((__vector_size__(8)));
+
+// Kernel parameters (passed by value).
+struct KParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* rab;
+  void* out;
+  const int32_t* seq_offsets;
+  const int32_t* num_context;
+  const int32_t* num_targets;
+  const void* kv_cache;
+  const int32_t* page_offsets;
+  const int32_t* page_ids;
+  const int32_t* last_page_len;
+  int32_t* items;     // work list, (b << 16) | q_tile
+  int32_t* n_items;   // number of valid list entries
+  int32_t* counter;   // work-queue head
+  int32_t* exited;    // workgroups that left the queue (the last one resets both counters)
+  int32_t batch;
+  int32_t max_seq_len;
+  int32_t Hq;
+  int32_t Hk;
+  int32_t group;      // Hq / Hk
+  int32_t hpw_log2;   // log2(query heads per workgroup)
+  int32_t n_hg;       // Hq >> hpw_log2
+  int32_t bm;         // query rows per item = 32 * (4 >> hpw_log2)
+  int32_t n_qt_max;   // q tiles per sequence, upper bound
+  int32_t ps_log2;    // log2(page_size)
+  int32_t g;          // target_group_size
+  int32_t rab_vec;    // rab rows allow 4-element vector loads
+  float alpha;
+  float c_exp;        // exponent scale, see epilogue
+  float out_mul;      // final scale of O
+};
+
+// ------------------------------------------------------------------------
+// Sequence geometry and the mask
+// ------------------------------------------------------------------------
+struct Seq {
+  int q_tok0;  // row of query 0 in q / out
+  int k_tok0;  // row of key position Lh in k / v (jagged: position 0)
+  int Lq;      // queries of this sequence
+  int Lh;      // absolute position of query 0 (paged history length, else 0)
+  int L;       // key positions 0 .. L-1
+  int H;       // first target position (L - clamped num_targets)
+  int nc;      // clamped num_context
+  int page0;   // first page_ids entry (paged)
+};
+
+template <bool PAGED>
+__device__ inline Seq load_seq(const KParams& p, int b, bool causal) {
+  Seq s;
+  const int o0 = p.seq_offsets[b], o1 = p.seq_offsets[b + 1];
+  s.q_tok0 = o0;
+  s.k_tok0 = o0;
+  s.Lq = o1 - o0;
+  s.page0 = 0;
+  s.Lh = 0;
+  if (PAGED) {
+    const int pg0 = p.page_offsets[b], pg1 = p.page_offsets[b + 1];
+    s.page0 = pg0;
+    s.Lh = pg1 > pg0 ? ((pg1 - pg0 - 1) << p.ps_log2) + p.last_page_len[b] : 0;
+  }
+  s.L = s.Lh + s.Lq;
+  int nt = (causal && p.num_targets) ? p.num_targets[b] : 0;
+  nt = min(max(nt, 0), s.L);
+  s.H = s.L - nt;
+  int nc = (causal && p.num_context) ? p.num_context[b] : 0;
+  s.nc = min(max(nc, 0), s.H);
+  return s;
+}
+
+// Key tiles that are not fully masked for the query rows [i_lo, i_hi]
+// (absolute positions): tiles [0, ta) then [tb0, tb1).
+// Rows below H see keys up to max(i, nc - 1); target rows see all of
+// [0, H) and, causally, their own group of g targets (all targets if g = 0).
+struct Tiles {
+  int ta, tb0, tb1;
+};
+
+__device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, bool causal, int bn) {
+  Tiles t;
+  if (!causal) {
+    t.ta = (s.L + bn - 1) / bn;
+    t.tb0 = t.tb1 = t.ta;
+    return t;
+  }
+  int a_end, b_lo = 0, b_end = 0;
+  if (i_hi < s.H) {
+    a_end = max(i_hi + 1, i_lo < s.nc ? s.nc : 0);
+  } else if (g <= 0) {
+    a_end = i_hi + 1;
+  } else {
+    a_end = s.H;
+    b_lo = s.H + ((max(i_lo, s.H) - s.H) / g) * g;
+    b_end = i_hi + 1;
+  }
+  t.ta = (a_end + bn - 1) / bn;
+  t.tb0 = max(b_lo / bn, t.ta);
+  t.tb1 = max((b_end + bn - 1) / bn, t.tb0);
+  return t;
+}
+
+// ------------------------------------------------------------------------
+// Planner: counting sort of (sequence, q tile) items by visible key tiles.
+// ------------------------------------------------------------------------
+template <bool PAGED>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, int causal) {
+  __shared__ int hist[kMaxBins];
+  __shared__ int scan[2][kMaxBins];
+  __shared__ int count;
+  const int tid = threadIdx.x;
+  hist[tid] = 0;
+  if (tid == 0) count = 0;
+  __syncthreads();
+  const int total = p.batch * p.n_qt_max;
+  for (int idx = tid; idx < total; idx += kPlanThreads) {
+    const int b = idx / p.n_qt_max, qt = idx - b * p.n_qt_max;
+    const Seq s = load_seq<PAGED>(p, b, causal != 0);
+    const int q_lo = qt * p.bm;
+    if (q_lo >= s.Lq) continue;
+    const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
+    const Tiles t = tile_range(s, i_lo, i_hi, p.g, causal != 0, bn);
+    const int cost = min(t.ta + t.tb1 - t.tb0, kMaxBins - 1);
+    atomicAdd(&hist[cost], 1);
+    atomicAdd(&count, 1);
+  }
+  __syncthreads();
+  // Exclusive scan over bins in descending cost: start[c] = sum of hist[c'] for c' > c.
+  int buf = 0;
+  scan[0][tid] = tid == 0 ? 0 : hist[kMaxBins - tid];
+  __syncthreads();
+  for (int off = 1; off < kMaxBins; off <<= 1) {
+    int x = scan[buf][tid];
+    if (tid >= off) x += scan[buf][tid - off];
+    scan[buf ^ 1][tid] = x;
+    buf ^= 1;
+    __syncthreads();
+  }
+  hist[tid] = scan[buf][kMaxBins - 1 - tid];
+  __syncthreads();
+  for (int idx = tid; idx < total; idx += kPlanThreads) {
+    const int b = idx / p.n_qt_max, qt = idx - b * p.n_qt_max;
+    const Seq s = load_seq<PAGED>(p, b, causal != 0);
+    const int q_lo = qt * p.bm;
+    if (q_lo >= s.Lq) continue;
+    const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
+    const Tiles t = tile_range(s, i_lo, i_hi, p.g, causal != 0, bn);
+    const int cost = min(t.ta + t.tb1 - t.tb0, kMaxBins - 1);
+    const int pos = atomicAdd(&hist[cost], 1);
+    p.items[pos] = (b << 16) | qt;
+  }
+  if (tid == 0) {
+    *p.n_items = count;
+    *p.counter = 0;
+    *p.exited = 0;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Helpers
+// ------------------------------------------------------------------------
+template <typename T>
+struct Frag;
+template <>
+struct Frag<__bf16> {
+  using v8 = bf16x8_t;
+  static constexpr bool fold_alpha = true;  // bf16 keeps fp32's range
+  __device__ static inline f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Frag<_Float16> {
+  using v8 = f16x8_t;
+  static constexpr bool fold_alpha = false;  // keep P = silu(alpha*S) inside fp16 range
+  __device__ static inline f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T>
+__device__ inline float to_f32(T x) {
+  return (float)x;
+}
+
+// Four packed 16-bit values -> fp32.
+template <typename T>
+__device__ inline void load4_f32(u32x2_t x, float* out) {
+  if constexpr (std::is_same<T, __bf16>::value) {
+    out[0] = __builtin_bit_cast(float, x[0] << 16);
+    out[1] = __builtin_bit_cast(float, x[0] & 0xffff0000u);
+    out[2] = __builtin_bit_cast(float, x[1] << 16);
+    out[3] = __builtin_bit_cast(float, x[1] & 0xffff0000u);
+  } else {
+    const T* t = (const T*)&x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = (float)t[e];
+  }
+}
+
+// Key position j -> pointer to its K (which = 0) or V (which = 1) row of kv head hk.
+template <typename T, int D, bool PAGED>
+__device__ inline const T* kv_row(const KParams& p, const Seq& s, int hk, int j, int which) {
+  if (PAGED) {
+    if (j < s.Lh) {
+      const int page = p.page_ids[s.page0 + (j >> p.ps_log2)];
+      const int slot = j & ((1 << p.ps_log2) - 1);
+      const size_t row = ((((size_t)page * 2 + which) << p.ps_log2) + slot) * p.Hk + hk;
+      return (const T*)p.kv_cache + row * D;
+    }
+    j -= s.Lh;
+  }
+  return (const T*)(which ? p.v : p.k) + ((size_t)(s.k_tok0 + j) * p.Hk + hk) * D;
+}
+
+// Position of key k (0 <= k < tile) in a V^T row: bits 2 and 3 swapped.
+__device__ inline int vt_pos(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+__device__ inline int next_item(int* sh, int* counter) {
+  __syncthreads();
+  if (threadIdx.x == 0) *sh = atomicAdd(counter, 1);
+  __syncthreads();
+  return *sh;
+}
+
+// Called by every workgroup after its last (failed) queue pop. Every
+// workgroup has popped for the last time before the final one arrives, so
+// that one can rewind the queue for the next run of the same plan.
+__device__ inline void leave_queue(const KParams& p) {
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int done = atomicAdd(p.exited, 1);
+    if (done == (int)gridDim.x - 1) {
+      atomicExch(p.counter, 0);
+      atomicExch(p.exited, 0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// bf16 / fp16 forward
+// ------------------------------------------------------------------------
+template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void fwd_kernel(KParams p) {
+  using F = Frag<T>;
+  using V8 = typename F::v8;
+  constexpr int KS = D / 16;   // k steps of S^T = K Q^T
+  constexpr int NJB = BN / 32; // 32-key blocks per tile
+  constexpr int NDB = D / 32;  // 32-wide blocks of O^T
+  constexpr int KLD = D + 8;   // LDS row stride of K (elements)
+  constexpr int VLD = BN + 8;  // LDS row stride of V^T (elements)
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int K_CHUNKS = BN * CPR;
+  constexpr int K_PER_T = (K_CHUNKS + kThreads - 1) / kThreads;
+  constexpr int V_UNITS = (BN / 4) * CPR;  // 4 keys x 8 columns each
+  constexpr int V_PER_T = (V_UNITS + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) T Ks[BN * KLD];
+  __shared__ __attribute__((aligned(16))) T Vt[D * VLD];
+  __shared__ int sh_item;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int n_work = *p.n_items * p.n_hg;
+  const int hpw = 1 << p.hpw_log2;
+
+  for (int w = next_item(&sh_item, p.counter); w < n_work; w = next_item(&sh_item, p.counter)) {
+    const int item = w / p.n_hg;
+    const int hg = w - item * p.n_hg;
+    const int packed = p.items[item];
+    const int b = packed >> 16, qt = packed & 0xffff;
+    const Seq s = load_seq<PAGED>(p, b, CAUSAL);
+    const int h = hg * hpw + (wave & (hpw - 1));
+    const int rb = wave >> p.hpw_log2;
+    const int hk = (hg * hpw) / p.group;
+    const int q_lo = qt * p.bm;
+    const int q_hi = min(q_lo + p.bm, s.Lq);
+    const int i_lo = s.Lh + q_lo, i_hi = s.Lh + q_hi - 1;
+    const int q_loc = q_lo + rb * kRowsPerWave + l32;
+    const bool row_ok = q_loc < s.Lq;
+    const bool wave_active = q_lo + rb * kRowsPerWave < s.Lq;
+    const int i = s.Lh + q_loc;
+
+    // Q fragments: B operand of S^T = K Q^T (lane: query l32, 8 features per k step).
+    V8 qf[KS];
+    {
+      const T* qrow = (const T*)p.q + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (row_ok) x = *(const u32x4_t*)(qrow + ks * 16);
+        qf[ks] = __builtin_bit_cast(V8, x);
+      }
+    }
+    // Per-lane mask bounds: key j < H is visible iff j <= hi_i; key j >= H iff tlo_i <= j <= i.
+    const int hi_i = (i < s.nc) ? max(i, s.nc - 1) : i;
+    const int tlo_i = (p.g <= 0) ? s.H : (i >= s.H ? s.H + ((i - s.H) / p.g) * p.g : INT_MAX);
+
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
+    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
+
+    u32x4_t kreg[K_PER_T];
+    u32x4_t vreg[V_PER_T][4];
+    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    auto load_tile = [&](int kt) {
+      const int j0 = kt * BN;
+#pragma unroll
+      for (int u = 0; u < K_PER_T; ++u) {
+        const int c = tid + u * kThreads;
+        const int r = c / CPR, col = c % CPR;
+        const int j = j0 + r;
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if ((K_CHUNKS % kThreads == 0 || c < K_CHUNKS) && j < s.L)
+          x = *(const u32x4_t*)(kv_row<T, D, PAGED>(p, s, hk, j, 0) + col * 8);
+        kreg[u] = x;
+      }
+#pragma unroll
+      for (int u = 0; u < V_PER_T; ++u) {
+        const int c = tid + u * kThreads;
+        const int kg = c / CPR, col = c % CPR;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int j = j0 + kg * 4 + rr;
+          u32x4_t x = {0u, 0u, 0u, 0u};
+          if ((V_UNITS % kThreads == 0 || c < V_UNITS) && j < s.L)
+            x = *(const u32x4_t*)(kv_row<T, D, PAGED>(p, s, hk, j, 1) + col * 8);
+          vreg[u][rr] = x;
+        }
+      }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+      for (int u = 0; u < K_PER_T; ++u) {
+        const int c = tid + u * kThreads;
+        if (K_CHUNKS % kThreads == 0 || c < K_CHUNKS) {
+          const int r = c / CPR, col = c % CPR;
+          *(u32x4_t*)&Ks[r * KLD + col * 8] = kreg[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < V_PER_T; ++u) {
+        const int c = tid + u * kThreads;
+        if (V_UNITS % kThreads == 0 || c < V_UNITS) {
+          const int kg = c / CPR, col = c % CPR;
+          const int pos = vt_pos(kg * 4);
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t a0 = vreg[u][0][wd], a1 = vreg[u][1][wd], a2 = vreg[u][2][wd], a3 = vreg[u][3][wd];
+            u32x2_t lo, hi;
+            lo[0] = (a0 & 0xffffu) | (a1 << 16);
+            lo[1] = (a2 & 0xffffu) | (a3 << 16);
+            hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+            hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+            *(u32x2_t*)&Vt[(col * 8 + 2 * wd) * VLD + pos] = lo;
+            *(u32x2_t*)&Vt[(col * 8 + 2 * wd + 1) * VLD + pos] = hi;
+          }
+        }
+      }
+    };
+
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+    if (n_tiles > 0) load_tile(tile_at(0));
+    for (int n = 0; n < n_tiles; ++n) {
+      const int kt = tile_at(n);
+      __syncthreads();
+      store_tile();
+      __syncthreads();
+      if (n + 1 < n_tiles) load_tile(tile_at(n + 1));
+      if (!wave_active) continue;
+      const int j0 = kt * BN;
+
+      float rv[NJB][16];
+      if (RAB) {
+        const T* rrow = (const T*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + q_loc) * p.max_seq_len;
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int jj = j0 + jb * 32 + 8 * a + 4 * half;
+            if (row_ok && jj + 3 < s.L && p.rab_vec) {
+              const u32x2_t x = *(const u32x2_t*)(rrow + jj);
+              load4_f32<T>(x, &rv[jb][4 * a]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) rv[jb][4 * a + e] = (row_ok && jj + e < s.L) ? to_f32(rrow[jj + e]) : 0.f;
+            }
+          }
+      }
+
+      // S^T = K Q^T: lane holds query l32 and keys j0 + 32 jb + 8 (r/4) + 4 half + r%4.
+      f32x16_t sacc[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const V8 a = *(const V8*)&Ks[(jb * 32 + l32) * KLD + ks * 16 + half * 8];
+          sacc[jb] = F::mfma(a, qf[ks], sacc[jb]);
+        }
+      }
+
+      // Epilogue: rab, alpha, SiLU, mask (partial tiles only), round to T.
+      const int j1 = min(j0 + BN, s.L);
+      const bool full = !CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc));
+      V8 pf[NJB][2];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[jb][r];
+          if (RAB) x += rv[jb][r];
+          if (!F::fold_alpha) x *= p.alpha;
+          const float e = __builtin_amdgcn_exp2f(x * p.c_exp);
+          float pv = x * __builtin_amdgcn_rcpf(1.f + e);
+          if (CAUSAL && !full) {
+            const int j = j0 + jb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+            const bool vis = (j < s.H) ? (j <= hi_i) : (j >= tlo_i && j <= i);
+            pv = vis ? pv : 0.f;
+          }
+          pf[jb][r / 8][r % 8] = (T)pv;
+        }
+      }
+
+      // O^T += V^T P^T: A = V^T rows (d = l32), B = P from registers.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const V8 a = *(const V8*)&Vt[(db * 32 + l32) * VLD + jb * 32 + 16 * m + 8 * half];
+            o[db] = F::mfma(a, pf[jb][m], o[db]);
+          }
+    }
+
+    // Store: lane holds query l32, features d = 32 db + 8 a + 4 half + 0..3.
+    if (row_ok) {
+      T* orow = (T*)p.out + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          T y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (T)(o[db][4 * a + e] * p.out_mul);
+          *(u32x2_t*)(orow + db * 32 + 8 * a + 4 * half) = *(const u32x2_t*)y;
+        }
+    }
+  }
+  leave_queue(p);
+}
+
+// ------------------------------------------------------------------------
+// fp32 forward (v_mfma_f32_32x32x2f32). Same structure; V stays row-major in
+// LDS because each k step of the second product takes one key per half-wave.
+// ------------------------------------------------------------------------
+template <int D, int BN, bool CAUSAL, bool RAB, bool PAGED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void fwd_kernel_f32(KParams p) {
+  using T = float;
+  constexpr int KH = D / 2;    // features per half-wave; k step ks uses feature half*KH + ks
+  constexpr int NJB = BN / 32;
+  constexpr int NDB = D / 32;
+  constexpr int KLD = D + 4;
+  constexpr int VLD = D;
+  constexpr int CPR = D / 4;   // 16-byte chunks per row
+  constexpr int CHUNKS = BN * CPR;
+  constexpr int PER_T = (CHUNKS + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) float Ks[BN * KLD];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * VLD];
+  __shared__ int sh_item;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int n_work = *p.n_items * p.n_hg;
+  const int hpw = 1 << p.hpw_log2;
+
+  for (int w = next_item(&sh_item, p.counter); w < n_work; w = next_item(&sh_item, p.counter)) {
+    const int item = w / p.n_hg;
+    const int hg = w - item * p.n_hg;
+    const int packed = p.items[item];
+    const int b = packed >> 16, qt = packed & 0xffff;
+    const Seq s = load_seq<PAGED>(p, b, CAUSAL);
+    const int h = hg * hpw + (wave & (hpw - 1));
+    const int rb = wave >> p.hpw_log2;
+    const int hk = (hg * hpw) / p.group;
+    const int q_lo = qt * p.bm;
+    const int q_hi = min(q_lo + p.bm, s.Lq);
+    const int i_lo = s.Lh + q_lo, i_hi = s.Lh + q_hi - 1;
+    const int q_loc = q_lo + rb * kRowsPerWave + l32;
+    const bool row_ok = q_loc < s.Lq;
+    const bool wave_active = q_lo + rb * kRowsPerWave < s.Lq;
+    const int i = s.Lh + q_loc;
+
+    float qf[KH];
+    {
+      const float* qrow = (const float*)p.q + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D + half * KH;
+#pragma unroll
+      for (int c = 0; c < KH / 4; ++c) {
+        f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok) x = *(const f32x4_t*)(qrow + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * c + e] = x[e];
+      }
+    }
+    const int hi_i = (i < s.nc) ? max(i, s.nc - 1) : i;
+    const int tlo_i = (p.g <= 0) ? s.H : (i >= s.H ? s.H + ((i - s.H) / p.g) * p.g : INT_MAX);
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
+    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
+
+    f32x4_t kreg[PER_T], vreg[PER_T];
+    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    auto load_tile = [&](int kt) {
+      const int j0 = kt * BN;
+#pragma unroll
+      for (int u = 0; u < PER_T; ++u) {
+        const int c = tid + u * kThreads;
+        const int r = c / CPR, col = c % CPR;
+        const int j = j0 + r;
+        f32x4_t xk = {0.f, 0.f, 0.f, 0.f}, xv = {0.f, 0.f, 0.f, 0.f};
+        if ((CHUNKS % kThreads == 0 || c < CHUNKS) && j < s.L) {
+          xk = *(const f32x4_t*)(kv_row<float, D, PAGED>(p, s, hk, j, 0) + col * 4);
+          xv = *(const f32x4_t*)(kv_row<float, D, PAGED>(p, s, hk, j, 1) + col * 4);
+        }
+        kreg[u] = xk;
+        vreg[u] = xv;
+      }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+      for (int u = 0; u < PER_T; ++u) {
+        const int c = tid + u * kThreads;
+        if (CHUNKS % kThreads == 0 || c < CHUNKS) {
+          const int r = c / CPR, col = c % CPR;
+          *(f32x4_t*)&Ks[r * KLD + col * 4] = kreg[u];
+          *(f32x4_t*)&Vs[r * VLD + col * 4] = vreg[u];
+        }
+      }
+    };
+
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+    if (n_tiles > 0) load_tile(tile_at(0));
+    for (int n = 0; n < n_tiles; ++n) {
+      const int kt = tile_at(n);
+      __syncthreads();
+      store_tile();
+      __syncthreads();
+      if (n + 1 < n_tiles) load_tile(tile_at(n + 1));
+      if (!wave_active) continue;
+      const int j0 = kt * BN;
+
+      f32x16_t sacc[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < KH / 4; ++c) {
+          const f32x4_t a4 = *(const f32x4_t*)&Ks[(jb * 32 + l32) * KLD + half * KH + 4 * c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], qf[4 * c + e], sacc[jb], 0, 0, 0);
+        }
+      }
+
+      const int j1 = min(j0 + BN, s.L);
+      const bool full = !CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc));
+      const float* rrow =
+          RAB ? (const float*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + q_loc) * p.max_seq_len : nullptr;
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + jb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+          float x = sacc[jb][r];
+          if (RAB) x += (row_ok && j < s.L) ? rrow[j] : 0.f;
+          const float e = __builtin_amdgcn_exp2f(x * p.c_exp);
+          float pv = x * __builtin_amdgcn_rcpf(1.f + e);
+          if (CAUSAL && !full) {
+            const bool vis = (j < s.H) ? (j <= hi_i) : (j >= tlo_i && j <= i);
+            pv = vis ? pv : 0.f;
+          }
+          sacc[jb][r] = pv;
+        }
+
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float a = Vs[(jb * 32 + 8 * (r / 4) + 4 * half + (r % 4)) * VLD + db * 32 + l32];
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[jb][r], o[db], 0, 0, 0);
+          }
+    }
+
+    if (row_ok) {
+      float* orow = (float*)p.out + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4_t y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = o[db][4 * a + e] * p.out_mul;
+          *(f32x4_t*)(orow + db * 32 + 8 * a + 4 * half) = y;
+        }
+    }
+  }
+  leave_queue(p);
+}
+
+// ------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------
+constexpr size_t kHeaderBytes = 256;
+
+int heads_per_wg_log2(int group) {
+  if (group % 4 == 0) return 2;
+  if (group % 2 == 0) return 1;
+  return 0;
+}
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+using KernelFn = void (*)(KParams);
+
+template <typename T, int D, bool PAGED>
+KernelFn pick16(bool causal, bool rab) {
+  constexpr int BN = D >= 256 ? 32 : 64;
+  constexpr int WPE = D >= 256 ? 1 : 2;
+  if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE> : fwd_kernel<T, D, BN, false, false, true, WPE>;
+  if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE> : fwd_kernel<T, D, BN, true, false, false, WPE>;
+  return rab ? fwd_kernel<T, D, BN, false, true, false, WPE> : fwd_kernel<T, D, BN, false, false, false, WPE>;
+}
+
+template <int D, bool PAGED>
+KernelFn pick32(bool causal, bool rab) {
+  constexpr int BN = 64;
+  if (PAGED) return causal ? fwd_kernel_f32<D, BN, true, false, true> : fwd_kernel_f32<D, BN, false, false, true>;
+  if (causal) return rab ? fwd_kernel_f32<D, BN, true, true, false> : fwd_kernel_f32<D, BN, true, false, false>;
+  return rab ? fwd_kernel_f32<D, BN, false, true, false> : fwd_kernel_f32<D, BN, false, false, false>;
+}
+
+template <bool PAGED>
+KernelFn pick(DType dt, int D, bool causal, bool rab, int* bn, int* wpe) {
+  *bn = (dt != DType::F32 && D >= 256) ? 32 : 64;
+  *wpe = (dt == DType::F32 || D >= 256) ? 1 : 2;
+  switch (dt) {
+    case DType::BF16:
+      switch (D) {
+        case 32: return pick16<__bf16, 32, PAGED>(causal, rab);
+        case 64: return pick16<__bf16, 64, PAGED>(causal, rab);
+        case 128: return pick16<__bf16, 128, PAGED>(causal, rab);
+        case 256: return pick16<__bf16, 256, PAGED>(causal, rab);
+      }
+      break;
+    case DType::F16:
+      switch (D) {
+        case 32: return pick16<_Float16, 32, PAGED>(causal, rab);
+        case 64: return pick16<_Float16, 64, PAGED>(causal, rab);
+        case 128: return pick16<_Float16, 128, PAGED>(causal, rab);
+        case 256: return pick16<_Float16, 256, PAGED>(causal, rab);
+      }
+      break;
+    case DType::F32:
+      switch (D) {
+        case 32: return pick32<32, PAGED>(causal, rab);
+        case 64: return pick32<64, PAGED>(causal, rab);
+        case 128: return pick32<128, PAGED>(causal, rab);
+      }
+      break;
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
+                           int32_t head_dim, DType dtype) {
+  (void)head_dim;
+  (void)dtype;
+  if (batch < 0 || max_q_len < 0 || num_heads_q <= 0 || num_heads_kv <= 0) return 0;
+  const int group = num_heads_q / num_heads_kv;
+  const int bm = kRowsPerWave * (kWaves >> heads_per_wg_log2(group));
+  const size_t n_qt = ((size_t)max_q_len + bm - 1) / bm;
+  return kHeaderBytes + (size_t)batch * n_qt * sizeof(int32_t);
+}
+
+namespace {
+
+KParams make_params(const FwdArgs& a) {
+  KParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.rab = a.rab;
+  p.out = a.out;
+  p.seq_offsets = a.seq_offsets;
+  p.num_context = a.num_context;
+  p.num_targets = a.num_targets;
+  p.kv_cache = a.kv_cache;
+  p.page_offsets = a.page_offsets;
+  p.page_ids = a.page_ids;
+  p.last_page_len = a.last_page_len;
+  char* ws = (char*)a.workspace;
+  p.n_items = (int32_t*)ws;
+  p.counter = (int32_t*)(ws + 64);
+  p.exited = (int32_t*)(ws + 128);
+  p.items = (int32_t*)(ws + kHeaderBytes);
+  p.batch = a.batch;
+  p.max_seq_len = a.max_seq_len;
+  p.Hq = a.num_heads_q;
+  p.Hk = a.num_heads_kv;
+  p.group = a.num_heads_q / a.num_heads_kv;
+  p.hpw_log2 = heads_per_wg_log2(p.group);
+  p.n_hg = a.num_heads_q >> p.hpw_log2;
+  p.bm = kRowsPerWave * (kWaves >> p.hpw_log2);
+  p.n_qt_max = (a.max_seq_len + p.bm - 1) / p.bm;
+  int ps_log2 = 0;
+  while (a.paged && (1 << ps_log2) < a.page_size) ++ps_log2;
+  p.ps_log2 = ps_log2;
+  p.g = a.target_group_size;
+  p.rab_vec = (a.max_seq_len % 4) == 0;
+  p.alpha = a.alpha;
+  const bool fold = a.dtype != DType::F16;
+  p.c_exp = fold ? -a.alpha * kLog2e : -kLog2e;
+  p.out_mul = fold ? a.out_scale * a.alpha : a.out_scale;
+  return p;
+}
+
+int tile_n(const FwdArgs& a) { return (a.dtype != DType::F32 && a.head_dim >= 256) ? 32 : 64; }
+
+}  // namespace
+
+hipError_t launch_plan(const FwdArgs& a) {
+  const KParams p = make_params(a);
+  const int bn = tile_n(a);
+  if (a.paged)
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, a.stream, p, bn, a.causal ? 1 : 0);
+  else
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, a.stream, p, bn, a.causal ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_run(const FwdArgs& a) {
+  const KParams p = make_params(a);
+  int bn = 64, wpe = 2;
+  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, &bn, &wpe)
+                        : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, &bn, &wpe);
+  if (!fn) return hipErrorInvalidValue;
+  const long long upper = (long long)a.batch * p.n_qt_max * p.n_hg;
+  const long long cap = (long long)num_cus() * wpe;
+  const int grid = (int)(upper < cap ? upper : cap);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -72,7 +72,7 @@ typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2 } hstu_mask_t;
 
 /*
  * Workspace bytes hstu_fwd needs for these sizes (the work list of the tile
- * scheduler and the split-K partial sums). Returns 0 for invalid sizes.
+ * scheduler and its queue counters). Returns 0 for invalid sizes.
  */
 size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
                                int32_t head_dim, hstu_dtype_t dtype);
@@ -107,6 +107,36 @@ hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* 
                        void* stream /* hipStream_t */);
 
 /*
+ * hstu_fwd in two steps, for callers that time or reuse them separately
+ * (the work list depends only on the sequence layout and mask inputs, so
+ * stacked layers over the same batch can plan once and run many times).
+ *
+ * hstu_fwd_plan: the tile scheduler alone. It reads seq_offsets,
+ * num_context and num_targets on the device and writes into `workspace` a
+ * work list of (sequence, query tile) items, longest first (by the number of
+ * key tiles not fully masked), plus the queue counters the run consumes.
+ * Arguments and errors as hstu_fwd (q, k, v, rab, out are not needed).
+ *
+ * hstu_fwd_run: the fused forward kernel alone, consuming the plan held in
+ * `workspace`. The caller guarantees that the plan was made with the same
+ * seq_offsets contents, num_context, num_targets, batch, max_seq_len, head
+ * counts, head_dim, mask_type, target_group_size and dtype, and that no
+ * other call uses the workspace between the plan and the run. A run leaves
+ * the plan intact, so further runs may follow. hstu_fwd == plan + run.
+ */
+hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
+                            int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
+                            int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, hstu_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, void* out,
+                           const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
+                           int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
+                           int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
+                           float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                           void* stream /* hipStream_t */);
+
+/*
  * Workspace bytes hstu_fwd_paged needs. max_seq_len bounds history + new
  * tokens of every request. Returns 0 for invalid sizes.
  */
@@ -139,6 +169,25 @@ hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new
                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
                              int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
                              void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+
+/* hstu_fwd_paged in two steps, with the same contract as hstu_fwd_plan /
+ * hstu_fwd_run. The plan reads seq_offsets_q, page_offsets, last_page_len,
+ * num_context and num_targets; q, k_new, v_new, out, kv_cache and page_ids
+ * are needed by the run only. */
+hstu_status_t hstu_fwd_paged_plan(const int32_t* seq_offsets_q, const int32_t* page_offsets,
+                                  const int32_t* last_page_len, const int32_t* num_context, const int32_t* num_targets,
+                                  int32_t batch, int32_t page_size, int32_t max_seq_len, int32_t num_heads_q,
+                                  int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
+                                  int32_t target_group_size, hstu_dtype_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream /* hipStream_t */);
+
+hstu_status_t hstu_fwd_paged_run(const void* q, const void* k_new, const void* v_new, void* out,
+                                 const int32_t* seq_offsets_q, const void* kv_cache, const int32_t* page_offsets,
+                                 const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
+                                 const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
+                                 int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
+                                 int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /* Static description of a status code. Never NULL. */
 const char* hstu_status_string(hstu_status_t status);

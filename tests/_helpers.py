@@ -1,0 +1,106 @@
+"""Shared helpers of the GPU parity tests: run a case through the C ABI (via
+the binding) and through the float64 oracle, and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import hstu_jagged_attention_amd as hj
+import oracle
+
+# Tolerances: max-abs bars as stated for the workloads (1e-4 fp32, 2e-2
+# bf16/fp16 on unit-normal inputs), plus relative checks so that an
+# all-zero output cannot pass (out_scale = 1/max_seq_len makes |O| ~ 1e-2).
+TOL = {
+    "f32": dict(max_abs=1e-4, rel_l2=1e-5, rel_max=1e-3),
+    "f16": dict(max_abs=2e-2, rel_l2=1e-2, rel_max=2e-2),
+    "bf16": dict(max_abs=2e-2, rel_l2=1e-2, rel_max=2e-2),
+}
+
+
+def f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def gpu_device():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a visible GPU")
+    hj.load_library()
+    return torch.device("cuda:0")
+
+
+def run_jagged(c, dev, out=None, workspace=None, **over) -> torch.Tensor:
+    kw = dict(rab=None if c.rab is None else c.rab.to(dev), num_context=c.num_context, num_targets=c.num_targets,
+              max_seq_len=c.max_seq_len, mask_type=c.mask_type, target_group_size=c.target_group_size,
+              alpha=c.alpha, out_scale=c.out_scale, out=out, workspace=workspace)
+    kw.update(over)
+    return hj.hstu_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets), **kw)
+
+
+def run_paged(pc, dev, **over) -> torch.Tensor:
+    kw = dict(num_context=pc.num_context, num_targets=pc.num_targets, max_seq_len=pc.max_seq_len,
+              mask_type=pc.mask_type, target_group_size=pc.target_group_size, alpha=pc.alpha,
+              out_scale=pc.out_scale)
+    kw.update(over)
+    return hj.hstu_fwd_paged(pc.q.to(dev), pc.k_new.to(dev), pc.v_new.to(dev), pc.kv_cache.to(dev),
+                             torch.as_tensor(pc.seq_offsets_q), torch.as_tensor(pc.page_offsets),
+                             torch.as_tensor(pc.page_ids), torch.as_tensor(pc.last_page_len), **kw)
+
+
+def oracle_jagged(c, rows=None) -> np.ndarray:
+    return oracle.hstu_fwd(f64(c.q), f64(c.k), f64(c.v), c.seq_offsets, rab=None if c.rab is None else f64(c.rab),
+                           num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                           mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                           out_scale=c.out_scale, rows=rows)
+
+
+def oracle_jagged_sampled(c, picks):
+    """picks: {b: [(local_row, head), ...]}. Each sequence is handed to the
+    oracle on its own (the result of a sequence does not depend on the
+    others), so the oracle never needs the whole batch in float64.
+    Returns {b: (global token rows, heads, values [n, D])}."""
+    res = {}
+    for b, rows in picks.items():
+        s0, s1 = int(c.seq_offsets[b]), int(c.seq_offsets[b + 1])
+        rab = None if c.rab is None else f64(c.rab[b:b + 1])
+        vals = oracle.hstu_fwd(f64(c.q[s0:s1]), f64(c.k[s0:s1]), f64(c.v[s0:s1]), [0, s1 - s0], rab=rab,
+                               num_context=None if c.num_context is None else c.num_context[b:b + 1],
+                               num_targets=None if c.num_targets is None else c.num_targets[b:b + 1],
+                               max_seq_len=c.max_seq_len, mask_type=c.mask_type,
+                               target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale,
+                               rows=rows)
+        res[b] = (np.array([s0 + r for r, _ in rows]), np.array([h for _, h in rows]), vals)
+    return res
+
+
+def oracle_paged(pc, rows=None) -> np.ndarray:
+    return oracle.hstu_fwd_paged(f64(pc.q), f64(pc.k_new), f64(pc.v_new), f64(pc.kv_cache), pc.seq_offsets_q,
+                                 pc.page_offsets, pc.page_ids, pc.last_page_len, num_context=pc.num_context,
+                                 num_targets=pc.num_targets, mask_type=pc.mask_type,
+                                 target_group_size=pc.target_group_size, alpha=pc.alpha, out_scale=pc.out_scale,
+                                 rows=rows)
+
+
+def errors(got, ref):
+    g, r = f64(got), np.asarray(ref, dtype=np.float64)
+    d = np.abs(g - r)
+    max_abs = float(d.max()) if d.size else 0.0
+    ref_norm = float(np.linalg.norm(r))
+    rel_l2 = float(np.linalg.norm(g - r) / ref_norm) if ref_norm > 0 else float(np.linalg.norm(g - r))
+    ref_max = float(np.abs(r).max()) if r.size else 0.0
+    return max_abs, rel_l2, ref_max
+
+
+def assert_parity(got, ref, dtype: str, what: str = ""):
+    g = f64(got)
+    assert g.shape == np.shape(ref), (what, g.shape, np.shape(ref))
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    max_abs, rel_l2, ref_max = errors(g, ref)
+    t = TOL[dtype]
+    msg = f"{what}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} max|ref|={ref_max:.3e}"
+    assert max_abs <= t["max_abs"], msg
+    assert rel_l2 <= t["rel_l2"], msg
+    assert max_abs <= t["rel_max"] * max(ref_max, 1e-30) or max_abs == 0.0, msg
+    return max_abs, rel_l2

@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/hstu.h declares, and rejects bad arguments on the host before any
+launch. No call here reaches a kernel (each one fails validation first or is
+an empty input that launches nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hstu_jagged_attention_amd as hj
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+OK, INVAL, UNSUP, WS = hj.HSTU_OK, hj.HSTU_ERR_INVALID_ARG, hj.HSTU_ERR_UNSUPPORTED, hj.HSTU_ERR_WORKSPACE
+BF16, F16, F32 = 2, 1, 0
+FAKE = 0x10000  # 16-byte aligned host integer, never dereferenced (calls fail validation first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hj.load_library()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(hj.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = hj.status_string(code)
+        assert s.startswith("HSTU_")
+    assert "unknown" in hj.status_string(99)
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, rab=None, out=FAKE, off=FAKE, nc=None, nt=None, B=2, S=128, Hq=4, Hk=2, D=128,
+             mask=0, g=0, alpha=1.0, osc=1.0, dt=BF16, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.hstu_fwd(a["q"], a["k"], a["v"], a["rab"], a["out"], a["off"], a["nc"], a["nt"], a["B"], a["S"],
+                        a["Hq"], a["Hk"], a["D"], a["mask"], a["g"], a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"],
+                        a["stream"])
+
+
+def paged(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, out=FAKE, offq=FAKE, cache=FAKE, poff=FAKE, pids=FAKE, lpl=FAKE, nc=None,
+             nt=None, B=2, ps=64, S=128, Hq=4, Hk=4, D=128, mask=0, g=1, alpha=1.0, osc=1.0, dt=BF16, ws=FAKE,
+             wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.hstu_fwd_paged(a["q"], a["kn"], a["vn"], a["out"], a["offq"], a["cache"], a["poff"], a["pids"],
+                              a["lpl"], a["nc"], a["nt"], a["B"], a["ps"], a["S"], a["Hq"], a["Hk"], a["D"], a["mask"],
+                              a["g"], a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_empty_inputs_are_a_noop(lib):
+    # The page: a zero B, N or D means the operator does not run.
+    assert fwd(lib, B=0, q=None, k=None, v=None, out=None, off=None, ws=None, wsb=0) == OK
+    assert fwd(lib, Hq=0, q=None, k=None, v=None, out=None, off=None, ws=None, wsb=0) == OK
+    assert fwd(lib, D=0, q=None, k=None, v=None, out=None, off=None, ws=None, wsb=0) == OK
+    assert paged(lib, B=0, q=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hk=3), INVAL),                      # Hq not a multiple of Hk
+    (dict(Hk=0), INVAL),
+    (dict(B=-1), INVAL),
+    (dict(g=-1), INVAL),
+    (dict(S=0), INVAL),
+    (dict(S=20481), INVAL),
+    (dict(mask=1), UNSUP),                    # upper triangular: unsupported by the page itself
+    (dict(mask=3), UNSUP),                    # user mask tensor
+    (dict(mask=7), INVAL),
+    (dict(D=48), UNSUP),
+    (dict(D=256, dt=F32), UNSUP),
+    (dict(dt=5), UNSUP),
+    (dict(q=None), INVAL),
+    (dict(off=None), INVAL),
+    (dict(q=FAKE + 8), INVAL),                # not 16-byte aligned
+    (dict(rab=FAKE + 2), INVAL),
+    (dict(off=FAKE + 2), INVAL),
+    (dict(mask=2, nt=FAKE), INVAL),           # targets with the bidirectional mask
+    (dict(mask=2, nc=FAKE), INVAL),
+    (dict(ws=None), WS),
+    (dict(wsb=16), WS),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ps=48), UNSUP),
+    (dict(ps=512), UNSUP),
+    (dict(ps=-1), INVAL),
+    (dict(cache=None), INVAL),
+    (dict(pids=None), INVAL),
+    (dict(lpl=FAKE + 1), INVAL),
+    (dict(Hk=3), INVAL),
+    (dict(mask=3), UNSUP),
+    (dict(wsb=8), WS),
+])
+def test_paged_rejects(lib, kw, code):
+    assert paged(lib, **kw) == code
+
+
+def test_workspace_sizes(lib):
+    small = hj.hstu_fwd_workspace_size(8, 1024, 4, 4, 128, __import__("torch").bfloat16)
+    big = hj.hstu_fwd_workspace_size(8, 4096, 4, 4, 128, __import__("torch").bfloat16)
+    assert 0 < small < big
+    assert lib.hstu_fwd_workspace_size(2, 128, 4, 3, 128, BF16) == 0
+    assert lib.hstu_fwd_workspace_size(-1, 128, 4, 4, 128, BF16) == 0
+    assert lib.hstu_fwd_paged_workspace_size(64, 64, 4160, 4, 4, 128, BF16) > 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        hj.load_library(str(tmp_path / "missing.so"))

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs. CPU-sized cases are compared element by element;
+the full-size workloads, in the launch configuration the benchmark times,
+are compared on sampled rows."""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import hstu_jagged_attention_amd as hj
+from hstu_jagged_attention_amd import workloads as wl
+from _helpers import (assert_parity, f64, gpu_device, oracle_jagged, oracle_jagged_sampled, oracle_paged, run_jagged,
+                      run_paged)
+
+pytestmark = pytest.mark.gpu
+CAUSAL, NONE = wl.MASK_CAUSAL, wl.MASK_NONE
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return gpu_device()
+
+
+# ------------------------------------------------------------ the five workloads, CPU-sized
+def test_tiny_fp32_bidirectional_full(dev):
+    c = wl.tiny_fp32_bidirectional()
+    say("tiny_fp32_bidirectional", c.lengths.tolist())
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), "f32", "C1")
+
+
+@pytest.mark.parametrize("name,batch", [("bf16_mha_causal", 3), ("bf16_rab_target", 2), ("fp16_gqa_causal", 2)])
+def test_workload_reduced_batch(dev, name, batch):
+    c = wl.WORKLOADS[name](batch=batch)
+    say(name, "batch", batch, c.lengths.tolist())
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), c.dtype, name)
+
+
+def test_paged_workload_reduced(dev):
+    pc = wl.bf16_paged_target(batch=6)
+    say("bf16_paged_target batch 6", pc.history_lengths.tolist(), pc.new_lengths.tolist())
+    got = run_paged(pc, dev)
+    assert_parity(got, oracle_paged(pc), "bf16", "C5 reduced")
+
+
+# ------------------------------------------------------------ full sizes, sampled rows
+def _picks(c, n_seq=3, n_rows=12, seed=0):
+    rng = np.random.default_rng(seed)
+    L = c.lengths
+    seqs = {int(np.argmax(L)), int(np.argmin(L))}
+    while len(seqs) < min(n_seq, c.batch):
+        seqs.add(int(rng.integers(c.batch)))
+    picks = {}
+    for b in sorted(seqs):
+        n = int(L[b])
+        rows = {0, n - 1, n // 2}
+        if c.num_targets is not None:
+            nt = min(int(c.num_targets[b]), n)
+            rows |= {n - nt, max(n - nt - 1, 0)}
+        if c.num_context is not None:
+            rows |= {max(min(int(c.num_context[b]), n) - 1, 0)}
+        while len(rows) < min(n_rows, n):
+            rows.add(int(rng.integers(n)))
+        picks[b] = [(r, h) for r in sorted(rows) for h in range(c.num_heads_q)]
+    return picks
+
+
+@pytest.mark.parametrize("name", ["bf16_mha_causal", "bf16_rab_target", "fp16_gqa_causal"])
+def test_workload_full_size_sampled(dev, name):
+    c = wl.WORKLOADS[name]()
+    say(name, "full size: B", c.batch, "T", int(c.seq_offsets[-1]))
+    got = run_jagged(c, dev).cpu()
+    ref = oracle_jagged_sampled(c, _picks(c))
+    for b, (toks, heads, vals) in ref.items():
+        assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, c.dtype, f"{name} seq {b}")
+
+
+def test_paged_workload_full_size_sampled(dev):
+    pc = wl.bf16_paged_target()
+    say("bf16_paged_target full size: B", pc.batch, "Tq", int(pc.seq_offsets_q[-1]))
+    got = run_paged(pc, dev).cpu()
+    rng = np.random.default_rng(3)
+    reqs = set(rng.choice(pc.batch, 6, replace=False).tolist()) | {int(np.argmax(pc.history_lengths))}
+    rows = []
+    for b in sorted(reqs):
+        q0, q1 = int(pc.seq_offsets_q[b]), int(pc.seq_offsets_q[b + 1])
+        for t in sorted({q0, q1 - 1, (q0 + q1) // 2}):
+            rows += [(t, h) for h in range(pc.num_heads_q)]
+    ref = oracle_paged(pc, rows=rows)
+    idx_t = torch.as_tensor([t for t, _ in rows])
+    idx_h = torch.as_tensor([h for _, h in rows])
+    assert_parity(got[idx_t, idx_h], ref, "bf16", "C5 full sampled")
+
+
+# ------------------------------------------------------------ edge cases
+EDGE = [
+    # (name, lengths, Hq, Hk, D, dtype, mask, nc, nt, g, rab, S)
+    ("single_token_seqs", [1, 1, 3], 2, 2, 64, "bf16", CAUSAL, None, None, 0, False, None),
+    ("empty_seqs_inside", [0, 37, 0, 129, 0], 2, 1, 64, "bf16", CAUSAL, 3, 5, 1, True, None),
+    ("ragged_tails", [31, 33, 65, 127, 129, 200], 4, 4, 128, "bf16", CAUSAL, None, None, 0, False, None),
+    ("bidirectional_ragged", [17, 130, 64], 2, 2, 128, "f16", NONE, None, None, 0, True, None),
+    ("context_targets_exceed_L", [10, 40, 70], 2, 2, 64, "bf16", CAUSAL, (5, 60), (20, 90), 1, True, None),
+    ("group_size_3", [90, 150], 4, 2, 128, "bf16", CAUSAL, (0, 10), (10, 40), 3, True, None),
+    ("group_size_0_with_targets", [90, 150], 4, 2, 128, "f16", CAUSAL, (0, 10), (10, 40), 0, False, None),
+    ("all_targets", [50, 80], 2, 2, 64, "bf16", CAUSAL, 0, 200, 2, False, None),
+    ("rab_odd_max_seq_len", [77, 101], 2, 2, 64, "bf16", CAUSAL, (0, 4), (1, 9), 1, True, 103),
+    ("gqa_group_2", [150, 270], 4, 2, 128, "bf16", CAUSAL, None, (1, 16), 1, False, None),
+    ("gqa_group_3", [150, 270], 6, 2, 64, "f16", CAUSAL, None, (1, 16), 1, True, None),
+    ("gqa_group_8", [150, 270], 8, 1, 128, "f16", CAUSAL, (0, 8), (1, 16), 1, False, None),
+    ("head_dim_32_bf16", [100, 260], 2, 2, 32, "bf16", CAUSAL, (0, 8), (1, 16), 1, True, None),
+    ("head_dim_256_bf16", [100, 260], 2, 2, 256, "bf16", CAUSAL, (0, 8), (1, 16), 1, True, None),
+    ("head_dim_256_f16", [70, 200], 4, 1, 256, "f16", NONE, None, None, 0, False, None),
+    ("fp32_causal_d64", [70, 150], 2, 2, 64, "f32", CAUSAL, (0, 8), (1, 16), 1, True, None),
+    ("fp32_gqa_d128", [70, 150], 4, 2, 128, "f32", CAUSAL, None, (1, 16), 2, False, None),
+    ("fp32_bidirectional_d32", [5, 300], 2, 1, 32, "f32", NONE, None, None, 0, True, None),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(dev, case):
+    name, lengths, Hq, Hk, D, dtype, mask, nc, nt, g, rab, S = case
+    c = wl.jagged_case(zlib.crc32(name.encode()) % (1 << 30), lengths, Hq, Hk, D, dtype, mask_type=mask, num_context=nc,
+                       num_targets=nt, target_group_size=g, rab_std=0.5 if rab else None, max_seq_len=S)
+    say(name, lengths, Hq, Hk, D, dtype)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), dtype, name)
+
+
+def test_every_row_is_written(dev):
+    c = wl.jagged_case(5, [45, 0, 200, 1], 4, 2, 128, "bf16", num_targets=(1, 9), target_group_size=1)
+    say("every_row_is_written")
+    out = torch.full(tuple(c.q.shape), float("nan"), dtype=c.q.dtype, device=dev)
+    got = run_jagged(c, dev, out=out)
+    assert torch.isfinite(got).all()
+    assert_parity(got, oracle_jagged(c), "bf16", "nan-prefilled out")
+
+
+def test_masked_rab_nan_is_never_read(dev):
+    c = wl.jagged_case(6, [130, 70], 2, 2, 128, "bf16", num_context=(2, 6), num_targets=(3, 9), target_group_size=1,
+                       rab_std=0.3, max_seq_len=140)
+    say("masked_rab_nan")
+    import oracle
+    clean = c.rab.clone()
+    poisoned = c.rab.clone()
+    for b in range(2):
+        L = int(c.lengths[b])
+        clean[b, :, L:, :] = 0
+        clean[b, :, :, L:] = 0
+        M = torch.as_tensor(oracle.mask_matrix(CAUSAL, L, int(c.num_context[b]), int(c.num_targets[b]), 1))
+        blk = poisoned[b, :, :L, :L]
+        blk[:, ~M] = float("nan")
+    a = run_jagged(c, dev, rab=clean.to(dev))
+    bq = run_jagged(c, dev, rab=poisoned.to(dev))
+    assert torch.isfinite(bq).all()
+    assert torch.equal(a, bq)
+
+
+def test_run_to_run_bitwise_deterministic(dev):
+    c = wl.bf16_rab_target(batch=3)
+    say("determinism")
+    a = run_jagged(c, dev)
+    b = run_jagged(c, dev)
+    assert torch.equal(a, b)
+
+
+def test_gqa_equals_repeated_mha_on_gpu(dev):
+    c = wl.jagged_case(7, [200, 90], 8, 2, 128, "f16", num_targets=(1, 9), target_group_size=1)
+    say("gqa_vs_mha")
+    a = run_jagged(c, dev)
+    krep = c.k.repeat_interleave(4, dim=1).contiguous().to(dev)
+    vrep = c.v.repeat_interleave(4, dim=1).contiguous().to(dev)
+    b = hj.hstu_fwd(c.q.to(dev), krep, vrep, torch.as_tensor(c.seq_offsets), num_targets=c.num_targets,
+                    max_seq_len=c.max_seq_len, target_group_size=1, alpha=c.alpha, out_scale=c.out_scale)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 128, 256])
+def test_paged_page_sizes(dev, page_size):
+    pc = wl.paged_case(30 + page_size, [0, 1, 63, 64, 65, 300], [3, 1, 7, 64, 2, 33], 4, 2, 128, "bf16",
+                       page_size=page_size, num_context=(0, 4), target_group_size=2, extra_pages=3)
+    say("paged page_size", page_size)
+    got = run_paged(pc, dev)
+    assert_parity(got, oracle_paged(pc), "bf16", f"paged ps={page_size}")
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("f32", 32), ("bf16", 256)])
+def test_paged_dtypes(dev, dtype, D):
+    pc = wl.paged_case(40, [100, 257], [5, 40], 2, 2, D, dtype, page_size=64, target_group_size=1)
+    say("paged", dtype, D)
+    got = run_paged(pc, dev)
+    assert_parity(got, oracle_paged(pc), dtype, f"paged {dtype} D={D}")
+
+
+def test_paged_equals_gathered_jagged_on_gpu(dev):
+    pc = wl.paged_case(41, [130, 64, 5], [9, 3, 12], 4, 4, 128, "bf16", page_size=64, num_context=(0, 3),
+                       target_group_size=1)
+    say("paged_vs_gathered")
+    got = run_paged(pc, dev).cpu()
+    kv = pc.kv_cache
+    ks, vs, qs, offs = [], [], [], [0]
+    for b in range(pc.batch):
+        Lh = int(pc.history_lengths[b])
+        pages = torch.as_tensor(pc.page_ids[pc.page_offsets[b]:pc.page_offsets[b + 1]])
+        pos = torch.arange(Lh)
+        q0, q1 = int(pc.seq_offsets_q[b]), int(pc.seq_offsets_q[b + 1])
+        ks.append(torch.cat([kv[pages[pos // 64], 0, pos % 64], pc.k_new[q0:q1]]))
+        vs.append(torch.cat([kv[pages[pos // 64], 1, pos % 64], pc.v_new[q0:q1]]))
+        qs.append(torch.cat([torch.zeros(Lh, 4, 128, dtype=pc.q.dtype), pc.q[q0:q1]]))
+        offs.append(offs[-1] + Lh + q1 - q0)
+    out = hj.hstu_fwd(torch.cat(qs).to(dev), torch.cat(ks).to(dev), torch.cat(vs).to(dev), torch.as_tensor(offs),
+                      num_context=pc.num_context, num_targets=pc.num_targets, max_seq_len=pc.max_seq_len,
+                      target_group_size=1, alpha=pc.alpha, out_scale=pc.out_scale).cpu()
+    for b in range(pc.batch):
+        Lh = int(pc.history_lengths[b])
+        q0, q1 = int(pc.seq_offsets_q[b]), int(pc.seq_offsets_q[b + 1])
+        a, bb = got[q0:q1].double(), out[offs[b] + Lh: offs[b + 1]].double()
+        assert (a - bb).abs().max().item() <= 2e-2 * max(bb.abs().max().item(), 1e-30)
+
+
+def test_page_running_case_shape(dev):
+    # GQA running case of the operator page: B=2, S=256, 8 q heads, 2 kv heads, D=64, fp16,
+    # offsets [0, 128, 256], causal, silu_scale 1/256; q holds 512 tokens, out has q's shape.
+    g = torch.Generator().manual_seed(0)
+    q = torch.randn(512, 8, 64, generator=g).half()
+    k = torch.randn(512, 2, 64, generator=g).half()
+    v = torch.randn(512, 2, 64, generator=g).half()
+    say("page running case")
+    out = hj.hstu_fwd(q.to(dev), k.to(dev), v.to(dev), torch.tensor([0, 128, 256]), max_seq_len=256,
+                      mask_type=CAUSAL, out_scale=1.0 / 256)
+    assert tuple(out.shape) == (512, 8, 64)
+    import oracle
+    ref = oracle.hstu_fwd(f64(q[:256]), f64(k[:256]), f64(v[:256]), [0, 128, 256], max_seq_len=256, mask_type=CAUSAL,
+                          out_scale=1.0 / 256)
+    assert_parity(out[:256], ref, "f16", "page running case")
