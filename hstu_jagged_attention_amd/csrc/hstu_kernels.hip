@@ -287,13 +287,25 @@ __device__ inline void leave_queue(const KParams& p) {
 // and the constant -1/log2(e) joins out_scale in the final store, leaving
 // exp2, add, rcp, mul and a packed convert per element.
 // ------------------------------------------------------------------------
+// Chunk-slot swizzle of key row j. For D = 128 (16 chunks of 16 bytes, one
+// row = all 64 banks) it is 4 (j % 4) + (j / 4) % 4: the 16 rows a 16-lane
+// K-fragment read touches get 16 different slots, and the 4 rows x 4
+// chunks a 32-lane half of a transposing V read touches get 16 different
+// slots too. Other head dims keep the low bits that fit their row width.
 template <int D>
 __device__ inline int swz(int j) {
   constexpr int CPR = D / 8;  // 16-byte chunks per row
-  return ((((j & 7) << 1) | ((j >> 3) & 1))) & (CPR - 1);
+  if constexpr (CPR >= 16) {
+    return ((j & 3) << 2) | ((j >> 2) & 3);
+  } else if constexpr (CPR == 8) {
+    return (j >> 1) & 7;  // two rows share the 64 banks
+  } else {
+    return (j >> 2) & 3;  // four rows share the 64 banks
+  }
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the
 // wave writes lds_base + 16 l (lds_base must be wave-uniform).
@@ -327,8 +339,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
   constexpr int KB_PER_TILE = TILE_B / 1024;  // 1 KB DMA blocks per tile
   constexpr int KB_PER_WAVE = (KB_PER_TILE + kWaves - 1) / kWaves;
   static_assert(TILE_B % 1024 == 0, "tile must be a whole number of 1 KB DMA blocks");
+  using Buf0 = std::integral_constant<int, 0>;
+  using Buf1 = std::integral_constant<int, 1>;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE_B];  // [buffer][K, V][tile]
+  // Separate objects per buffer: the compiler's alias analysis can then see
+  // that the DMA filling one buffer does not write the one being read, and
+  // does not wait for the prefetch before reading the current tile.
+  __shared__ __attribute__((aligned(1024))) char smem_k0[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_v0[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_k1[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_v1[TILE_B];
+  auto kv_smem = [&](auto bufc, int which) -> char* {
+    constexpr int B = decltype(bufc)::value;
+    if constexpr (B == 0) return which ? smem_v0 : smem_k0; else return which ? smem_v1 : smem_k1;
+  };
   __shared__ int sh_item;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -336,6 +360,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
   const int l32 = lane & 31, half = lane >> 5;
   const int n_work = *p.n_items * p.n_hg;
   const int hpw = 1 << p.hpw_log2;
+  const uint32_t row_stride_b = (uint32_t)p.Hk * ROW_B;  // bytes between key rows of one kv head
+
+  // DMA geometry of this lane, the same for every tile: lane `lane` of
+  // block `blk` fills LDS byte o = blk*1024 + lane*16 of a tile, i.e. row
+  // o / ROW_B and chunk slot (o % ROW_B) / 16, which holds global chunk
+  // slot ^ swz(row).
+  auto dma_row = [&](int u) { return ((wave * KB_PER_WAVE + u) * 1024 + lane * 16) / ROW_B; };
+  auto dma_col_b = [&](int u) {
+    const int o = (wave * KB_PER_WAVE + u) * 1024 + lane * 16;
+    return (uint32_t)((((o % ROW_B) / 16) ^ swz<D>(o / ROW_B)) * 16);
+  };
+  uint32_t dma_off_b[KB_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < KB_PER_WAVE; ++u) dma_off_b[u] = (uint32_t)dma_row(u) * row_stride_b + dma_col_b(u);
 
   for (int w = next_item(&sh_item, p.counter); w < n_work; w = next_item(&sh_item, p.counter)) {
     const int item = w / p.n_hg;
@@ -354,24 +392,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     const bool wave_active = q_lo + rb * kRowsPerWave < s.Lq;
     const int i = s.Lh + q_loc;
 
-    // DMA of key tile kt into buffer buf: lane `lane` of block `blk` fills
-    // LDS byte o = blk*1024 + lane*16 of the tile, i.e. row o / ROW_B, slot
-    // (o % ROW_B) / 16, which holds global chunk slot ^ swz(row). Rows past
-    // the sequence repeat its last row (finite values; masked to zero).
-    auto dma_tile = [&](int kt, int buf) {
+    // Uniform base addresses of a whole tile whose BN rows are consecutive
+    // rows of one tensor (stride row_stride_b); false for tiles that end past
+    // the sequence, straddle the history / new-token boundary, or span pages.
+    auto tile_bases = [&](int j0, const char*& kb, const char*& vb) -> bool {
+      if (!PAGED) {
+        if (j0 + BN > s.L) return false;
+        const size_t e = ((size_t)(s.k_tok0 + j0) * p.Hk + hk) * D;
+        kb = (const char*)((const T*)p.k + e);
+        vb = (const char*)((const T*)p.v + e);
+        return true;
+      } else {
+        if (j0 + BN <= s.Lh) {
+          if ((1 << p.ps_log2) < BN) return false;
+          const int page = p.page_ids[s.page0 + (j0 >> p.ps_log2)];
+          const size_t slot0 = (size_t)(j0 & ((1 << p.ps_log2) - 1));
+          const size_t ek = (((((size_t)page * 2) << p.ps_log2) + slot0) * p.Hk + hk) * D;
+          const size_t ev = (((((size_t)page * 2 + 1) << p.ps_log2) + slot0) * p.Hk + hk) * D;
+          kb = (const char*)((const T*)p.kv_cache + ek);
+          vb = (const char*)((const T*)p.kv_cache + ev);
+          return true;
+        }
+        if (j0 >= s.Lh && j0 + BN <= s.L) {
+          const size_t e = ((size_t)(s.k_tok0 + j0 - s.Lh) * p.Hk + hk) * D;
+          kb = (const char*)((const T*)p.k + e);
+          vb = (const char*)((const T*)p.v + e);
+          return true;
+        }
+        return false;
+      }
+    };
+    // DMA of key tile kt into buffer BUF. Rows past the sequence repeat its
+    // last row (finite values, masked to zero by the epilogue).
+    auto dma_tile = [&](int kt, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
       const int j0 = kt * BN;
+      const char *kb, *vb;
+      if (tile_bases(j0, kb, vb)) {
 #pragma unroll
-      for (int u = 0; u < KB_PER_WAVE; ++u) {
-        const int blk = wave * KB_PER_WAVE + u;
-        if (KB_PER_TILE % kWaves == 0 || blk < KB_PER_TILE) {
-          const int o = blk * 1024 + lane * 16;
-          const int r = o / ROW_B, slot = (o % ROW_B) / 16;
-          const int chunk = slot ^ swz<D>(r);
-          const int j = min(j0 + r, s.L - 1);
-          const T* krow = kv_row<T, D, PAGED>(p, s, hk, j, 0) + chunk * 8;
-          const T* vrow = kv_row<T, D, PAGED>(p, s, hk, j, 1) + chunk * 8;
-          dma16(krow, &smem[buf][0][blk * 1024]);
-          dma16(vrow, &smem[buf][1][blk * 1024]);
+        for (int u = 0; u < KB_PER_WAVE; ++u) {
+          const int blk = wave * KB_PER_WAVE + u;
+          if (KB_PER_TILE % kWaves == 0 || blk < KB_PER_TILE) {
+            dma16(kb + dma_off_b[u], kv_smem(bufc, 0) + blk * 1024);
+            dma16(vb + dma_off_b[u], kv_smem(bufc, 1) + blk * 1024);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < KB_PER_WAVE; ++u) {
+          const int blk = wave * KB_PER_WAVE + u;
+          if (KB_PER_TILE % kWaves == 0 || blk < KB_PER_TILE) {
+            const int j = min(j0 + dma_row(u), s.L - 1);
+            const char* krow = (const char*)kv_row<T, D, PAGED>(p, s, hk, j, 0) + dma_col_b(u);
+            const char* vrow = (const char*)kv_row<T, D, PAGED>(p, s, hk, j, 1) + dma_col_b(u);
+            dma16(krow, kv_smem(bufc, 0) + blk * 1024);
+            dma16(vrow, kv_smem(bufc, 1) + blk * 1024);
+          }
         }
       }
     };
@@ -408,11 +484,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
     const T* rrow = RAB ? (const T*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + q_loc) * p.max_seq_len : nullptr;
+    const int G = lane >> 4, sl = lane & 15;
 
-    if (n_tiles > 0) dma_tile(tile_at(0), 0);
-    for (int n = 0; n < n_tiles; ++n) {
+    // One key tile: publish its LDS buffer, request the next tile into the
+    // other buffer, then S^T, epilogue and O^T on this one.
+    auto step = [&](int n, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
       const int kt = tile_at(n);
-      const int buf = n & 1;
       wait_vmem_all();
       __syncthreads();
       const int j0 = kt * BN;
@@ -437,99 +515,172 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
             rv[jb][a] = x;
           }
       }
-      if (n + 1 < n_tiles) dma_tile(tile_at(n + 1), buf ^ 1);
-      if (!wave_active) continue;
+      if (n + 1 < n_tiles) dma_tile(tile_at(n + 1), std::integral_constant<int, BUF ^ 1>{});
+      if (!wave_active) return;
 
-      const char* kbuf = smem[buf][0];
-      const char* vbuf = smem[buf][1];
+      const char* kbuf = kv_smem(bufc, 0);
+      const char* vbuf = kv_smem(bufc, 1);
 
-      // S^T = c K Q^T: lane holds query l32, keys j0 + 32 jb + 8 (r/4) + 4 half + r%4.
-      f32x16_t sacc[NJB];
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
-        const int row = jb * 32 + l32;
-        const char* krow = kbuf + row * ROW_B;
-        const int sw = swz<D>(row);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const V8 a = *(const V8*)(krow + (((2 * ks + half) ^ sw) * 16));
-          sacc[jb] = F::mfma(a, qf[ks], sacc[jb]);
-        }
-      }
-
-      // Epilogue. Full tiles skip the mask; the branch is uniform.
+      // Full tiles skip the mask; the branch is uniform and taken once per
+      // tile, so each variant below is straight-line code the scheduler can
+      // interleave freely.
       const int j1 = min(j0 + BN, s.L);
       const bool full = (j0 + BN <= s.L) &&
                         (!CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc)));
+
+      // K fragment (A operand of S^T) for key block jb, k step ks.
+      auto k_frag = [&](int jb, int ks) -> V8 {
+        const int row = jb * 32 + l32;
+        return *(const V8*)(kbuf + row * ROW_B + (((2 * ks + half) ^ swz<D>(row)) * 16));
+      };
+      // V^T fragment (A operand of O^T += V^T P^T) for (jb, m, db): two
+      // transposing reads; the 16-lane group G = lane/16 reads key rows
+      // 32 jb + 16 m + 8 u + 4 (G/2) + (lane%16)/4 and features
+      // 32 db + 16 (G%2) + 4 (lane%4) .. +3, and lane t of the group receives
+      // feature 32 db + 16 (G%2) + t for those four keys.
+      auto v_frag = [&](int jb, int m, int db) -> V8 {
+        v4i16_t part[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int row = jb * 32 + 16 * m + 8 * u + 4 * (G >> 1) + (sl >> 2);
+          const int col = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+          part[u] = lds_read_tr16(vbuf + row * ROW_B + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2);
+        }
+        return __builtin_bit_cast(V8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+
+      // Mask bounds relative to the lane's first key of block jb.
+      int ma[NJB], mb[NJB], mc[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int jbase = j0 + jb * 32 + 4 * half;
+        ma[jb] = a_i - jbase;
+        mb[jb] = b_i == INT_MAX ? INT_MAX / 2 : b_i - jbase;
+        mc[jb] = i - jbase;
+      }
+      f32x16_t sacc[NJB];
       V8 pf[NJB][2];
-      auto epilogue = [&](auto masked) {
+      // Epilogue of element r of block jb: rab, mask (masked tiles), SiLU, round.
+      auto epi = [&](auto masked, int jb, int r) {
+        float y = sacc[jb][r];
+        if (RAB) {
+          const uint32_t wd = rv[jb][r / 4][(r % 4) / 2];
+          float rab_f;
+          if constexpr (std::is_same<T, __bf16>::value) {
+            rab_f = __builtin_bit_cast(float, (r % 2) ? (wd & 0xffff0000u) : (wd << 16));
+          } else {
+            const T* t2 = (const T*)&wd;
+            rab_f = (float)t2[r % 2];
+          }
+          y = __builtin_fmaf(rab_f, p.c_exp, y);
+        }
+        if constexpr (decltype(masked)::value) {
+          // Masked keys get y = +0 (bitwise AND), hence p = 0 * 1/2 = 0
+          // exactly, and a NaN rab there never reaches the arithmetic. Both
+          // variants run the same arithmetic otherwise, so results do not
+          // depend on which tiles a configuration classifies as full. With
+          // off = key offset inside the lane's 32-key block, key j is
+          // visible iff max(a_i - j, min(j - b_i, i - j)) >= 0.
+          const int off = 8 * (r / 4) + (r % 4);  // unrolled: a constant
+          const int v = max(ma[jb] - off, min(off - mb[jb], mc[jb] - off));
+          y = __builtin_bit_cast(float, __builtin_bit_cast(int, y) & ~(v >> 31));
+        }
+        const float e = __builtin_amdgcn_exp2f(y);
+        const float pv = y * __builtin_amdgcn_rcpf(1.f + e);
+        pf[jb][r / 8][r % 8] = (T)pv;
+      };
+
+      if constexpr (WPE == 1) {
+        // One wave per SIMD: overlap MFMA and VALU inside the wave. S^T of
+        // block jb runs while the epilogue of block jb - 1 fills the VALU
+        // slots; O^T of block 0 runs under the epilogue of the last block.
+        // Fragment reads are issued one step ahead. The full / masked choice
+        // selects one of two straight-line copies.
+        auto body = [&](auto masked) {
+          auto s_block = [&](int jb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
+            V8 kf = k_frag(jb, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              V8 kn = kf;
+              if (ks + 1 < KS) kn = k_frag(jb, ks + 1);
+              sacc[jb] = F::mfma(kf, qf[ks], sacc[jb]);
+              if (jb > 0) {
+#pragma unroll
+                for (int r = ks * 16 / KS; r < (ks + 1) * 16 / KS; ++r) epi(masked, jb - 1, r);
+              }
+              kf = kn;
+            }
+          };
+          auto pv_block = [&](int jb, bool overlap) {
+            constexpr int NSTEP = 2 * NDB;
+            V8 vf = v_frag(jb, 0, 0);
+#pragma unroll
+            for (int st = 0; st < NSTEP; ++st) {
+              const int m = st / NDB, db = st % NDB;
+              V8 vn = vf;
+              if (st + 1 < NSTEP) vn = v_frag(jb, (st + 1) / NDB, (st + 1) % NDB);
+              o[db] = F::mfma(vf, pf[jb][m], o[db]);
+              if (overlap) {
+#pragma unroll
+                for (int r = st * 16 / NSTEP; r < (st + 1) * 16 / NSTEP; ++r) epi(masked, NJB - 1, r);
+              }
+              vf = vn;
+            }
+          };
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) s_block(jb);
+          if (NJB > 1) {
+            pv_block(0, true);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) epi(masked, 0, r);
+            pv_block(0, false);
+          }
+#pragma unroll
+          for (int jb = 1; jb < NJB; ++jb) pv_block(jb, false);
+        };
+        if (full)
+          body(std::false_type{});
+        else
+          body(std::true_type{});
+      } else {
+        // Two waves per SIMD: keep the register footprint small and let the
+        // other workgroup on the SIMD fill the gaps; only the epilogue
+        // differs between full and masked tiles.
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float y = sacc[jb][r];
-            if (RAB) {
-              const uint32_t wd = rv[jb][r / 4][(r % 4) / 2];
-              float rab_f;
-              if constexpr (std::is_same<T, __bf16>::value) {
-                rab_f = __builtin_bit_cast(float, (r % 2) ? (wd & 0xffff0000u) : (wd << 16));
-              } else {
-                const T* t2 = (const T*)&wd;
-                rab_f = (float)t2[r % 2];
-              }
-              y = __builtin_fmaf(rab_f, p.c_exp, y);
-            }
-            if constexpr (decltype(masked)::value) {
-              // Masked keys get y = 0, hence p = 0 * 1/2 = 0 exactly (and a NaN
-              // rab there never reaches the arithmetic). Both variants then run
-              // the same instruction sequence, so results do not depend on
-              // which tiles a configuration classifies as full.
-              const int j = j0 + jb * 32 + 8 * (r / 4) + 4 * half + (r % 4);
-              const bool vis = (j <= a_i) || (j >= b_i && j <= i);
-              y = vis ? y : 0.f;
-            }
-            const float e = __builtin_amdgcn_exp2f(y);
-            const float pv = y * __builtin_amdgcn_rcpf(1.f + e);
-            pf[jb][r / 8][r % 8] = (T)pv;
-          }
+          for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) sacc[jb] = F::mfma(k_frag(jb, ks), qf[ks], sacc[jb]);
         }
-      };
-      if (full)
-        epilogue(std::false_type{});
-      else
-        epilogue(std::true_type{});
+        auto epi_all = [&](auto masked) {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) epi(masked, jb, r);
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        if (full)
+          epi_all(std::false_type{});
+        else
+          epi_all(std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] = F::mfma(v_frag(jb, m, db), pf[jb][m], o[db]);
+      }
+    };
 
-      // O^T += V^T P^T. A operand for (db, jb, m): two transposing reads; the
-      // 16-lane group G = lane/16 reads key rows jj + 8u + (lane%16)/4 and
-      // features 32 db + 16 (G%2) + 4 (lane%4) .. +3, and lane t of the group
-      // receives feature 32 db + 16 (G%2) + t for those four keys.
-      const int G = lane >> 4, sl = lane & 15;
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            v4i16_t part[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int row = jb * 32 + 16 * m + 8 * u + 4 * (G >> 1) + (sl >> 2);
-              const int col = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-              const char* addr = vbuf + row * ROW_B + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
-              part[u] = lds_read_tr16(addr);
-            }
-            V8 a;
-            const T* p0 = (const T*)&part[0];
-            const T* p1 = (const T*)&part[1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a[e] = p0[e];
-              a[4 + e] = p1[e];
-            }
-            o[db] = F::mfma(a, pf[jb][m], o[db]);
-          }
+    if (n_tiles > 0) dma_tile(tile_at(0), Buf0{});
+    for (int n = 0; n < n_tiles; n += 2) {
+      step(n, Buf0{});
+      if (n + 1 < n_tiles) step(n + 1, Buf1{});
     }
 
     // Store: lane holds query l32, features d = 32 db + 8 a + 4 half + 0..3.
@@ -742,7 +893,7 @@ using KernelFn = void (*)(KParams);
 template <typename T, int D, bool PAGED>
 KernelFn pick16(bool causal, bool rab) {
   constexpr int BN = D >= 256 ? 32 : 64;
-  constexpr int WPE = D >= 256 ? 1 : 2;
+  constexpr int WPE = PAGED ? 1 : (D >= 256 ? 1 : 2);
   if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE> : fwd_kernel<T, D, BN, false, false, true, WPE>;
   if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE> : fwd_kernel<T, D, BN, true, false, false, WPE>;
   return rab ? fwd_kernel<T, D, BN, false, true, false, WPE> : fwd_kernel<T, D, BN, false, false, false, WPE>;
@@ -759,7 +910,7 @@ KernelFn pick32(bool causal, bool rab) {
 template <bool PAGED>
 KernelFn pick(DType dt, int D, bool causal, bool rab, int* bn, int* wpe) {
   *bn = (dt != DType::F32 && D >= 256) ? 32 : 64;
-  *wpe = (dt == DType::F32 || D >= 256) ? 1 : 2;
+  *wpe = (dt == DType::F32 || D >= 256 || PAGED) ? 1 : 2;
   switch (dt) {
     case DType::BF16:
       switch (D) {
