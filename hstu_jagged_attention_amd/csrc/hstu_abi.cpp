@@ -57,14 +57,16 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
   if (batch < 0 || max_seq_len < 0 || num_heads_q < 0 || num_heads_kv < 0 || head_dim < 0) return 0;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return 256;
   if (num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
-  return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype));
+  return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype), false);
 }
 
 size_t hstu_fwd_paged_workspace_size(int32_t batch, int32_t page_size, int32_t max_seq_len, int32_t num_heads_q,
                                      int32_t num_heads_kv, int32_t head_dim, hstu_dtype_t dtype) {
-  if (page_size < 0) return 0;
+  if (page_size < 0 || batch < 0 || max_seq_len < 0 || num_heads_q < 0 || num_heads_kv < 0 || head_dim < 0) return 0;
+  if (batch == 0 || num_heads_q == 0 || head_dim == 0) return 256;
+  if (num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
   // New tokens per request are bounded by max_seq_len (history + new).
-  return hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, dtype);
+  return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype), true);
 }
 
 }  // extern "C"

@@ -41,17 +41,20 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
-// Bytes of workspace the launch needs (work list + queue counters).
+// Bytes of workspace a launch needs: work list, queue counters and, when
+// the launch may split long items over the key range, the split list and
+// the fp32 partial sums.
 size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, DType dtype);
+                           int32_t head_dim, DType dtype, bool paged);
 
 // Enqueues the planner on args.stream: it writes the work list into the
 // workspace and zeroes the work-queue counters.
 hipError_t launch_plan(const FwdArgs& args);
 
-// Enqueues the forward kernel on args.stream; it consumes the work list the
-// planner left in the workspace (same sizes and mask inputs) and leaves the
-// queue counters at zero when it ends, so one plan serves many runs.
+// Enqueues the forward kernel (and, for plans with split items, the split
+// reduction kernel) on args.stream; it consumes the work list the planner
+// left in the workspace (same sizes and mask inputs) and leaves the queue
+// counters at zero when it ends, so one plan serves many runs.
 hipError_t launch_run(const FwdArgs& args);
 
 }  // namespace hstu

@@ -67,8 +67,13 @@ struct KParams {
   const int32_t* page_offsets;
   const int32_t* page_ids;
   const int32_t* last_page_len;
-  int32_t* items;     // work list, (b << 16) | q_tile
+  int32_t* items;     // work list, two ints per entry (see the planner)
   int32_t* n_items;   // number of valid list entries
+  float* partials;    // split items: fp32 partial O, one slot per (chunk, head group)
+  int32_t* split_items;  // split items: two ints each (see the planner)
+  int32_t* n_split;      // number of split items
+  int32_t split_slots;   // partial-sum slots available (0: never split)
+  int32_t target_chunks; // chunks the planner aims for (about 2 per resident workgroup)
   int32_t* counter;   // work-queue head
   int32_t* exited;    // workgroups that left the queue (the last one resets both counters)
   int32_t batch;
@@ -157,28 +162,115 @@ __device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, bool
 }
 
 // ------------------------------------------------------------------------
-// Planner: counting sort of (sequence, q tile) items by visible key tiles.
+// Planner: (sequence, q tile) items, costed by visible key tiles, optionally
+// split into chunks of consecutive key tiles, counting-sorted longest first.
+//
+// Work list entry = two ints: (b << 16) | q_tile, and
+// (chunk << 24) | (n_chunks << 16) | slot, where `slot` is the first of the
+// n_chunks partial-sum slots of a split item (0xffff when not split).
+// Split items are also listed once each in the reduction list:
+// (b << 16) | q_tile, (n_chunks << 16) | slot.
+// Chunk size: the average work per resident workgroup (at least
+// kMinChunkTiles), doubled until the split items fit the partial-sum slots.
 // ------------------------------------------------------------------------
+// Wave-wide exclusive prefix sum of v (64 lanes); *total gets the wave sum.
+__device__ inline int wave_exclusive_sum(int v, int* total) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  *total = __shfl(x, 63, 64);
+  return x - v;
+}
+
+// Adds v of every lane to *counter with one atomic per wave; returns the
+// value of *counter before this lane's share (lanes in order).
+__device__ inline int wave_fetch_add(int* counter, int v) {
+  int total;
+  const int ex = wave_exclusive_sum(v, &total);
+  int base = 0;
+  if ((threadIdx.x & 63) == 63 && total != 0) base = atomicAdd(counter, total);
+  base = __shfl(base, 63, 64);
+  return base + ex;
+}
+
+constexpr int kMinChunkTiles = 4;
+constexpr int kCostCache = 4096;  // items whose cost the planner keeps in LDS
+
+__device__ inline int item_cost(const Tiles& t) { return t.ta + t.tb1 - t.tb0; }
+
 template <bool PAGED>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, int causal) {
-  __shared__ int hist[kMaxBins];
+  __shared__ int hist[kMaxBins];  // items per cost, then chunks per cost
   __shared__ int scan[2][kMaxBins];
-  __shared__ int count;
+  __shared__ short cost_cache[kCostCache];
+  __shared__ int count, total_cost, chunk_tiles, slot_alloc, n_split;
   const int tid = threadIdx.x;
+  const int n_items = p.batch * p.n_qt_max;
   hist[tid] = 0;
-  if (tid == 0) count = 0;
+  if (tid == 0) {
+    count = 0;
+    total_cost = 0;
+    slot_alloc = 0;
+    n_split = 0;
+  }
   __syncthreads();
-  const int total = p.batch * p.n_qt_max;
-  for (int idx = tid; idx < total; idx += kPlanThreads) {
+  auto compute_cost = [&](int idx) -> int {  // -1: no such item
     const int b = idx / p.n_qt_max, qt = idx - b * p.n_qt_max;
     const Seq s = load_seq<PAGED>(p, b, causal != 0);
     const int q_lo = qt * p.bm;
-    if (q_lo >= s.Lq) continue;
+    if (q_lo >= s.Lq) return -1;
     const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
-    const Tiles t = tile_range(s, i_lo, i_hi, p.g, causal != 0, bn);
-    const int cost = min(t.ta + t.tb1 - t.tb0, kMaxBins - 1);
-    atomicAdd(&hist[cost], 1);
-    atomicAdd(&count, 1);
+    return min(item_cost(tile_range(s, i_lo, i_hi, p.g, causal != 0, bn)), kMaxBins - 1);
+  };
+  auto cost_of = [&](int idx) -> int { return idx < kCostCache ? (int)cost_cache[idx] : compute_cost(idx); };
+  for (int base = 0; base < n_items; base += kPlanThreads) {  // uniform trip count: wave ops below
+    const int idx = base + tid;
+    const int c = idx < n_items ? compute_cost(idx) : -1;
+    if (idx < kCostCache && idx < n_items) cost_cache[idx] = (short)c;
+    if (c > 0) atomicAdd(&hist[c], 1);
+    wave_fetch_add(&total_cost, max(c, 0));
+  }
+  __syncthreads();
+  // Chunk size from the cost histogram (no further pass over the items):
+  // candidates t0, 2 t0, 4 t0, ... are evaluated together, one histogram
+  // bin per thread; the first whose split items fit the slots wins.
+  constexpr int kCand = 10;  // t0 << 9 >= kMaxBins: the last candidate never splits
+  __shared__ int need[kCand];
+  if (tid < kCand) need[tid] = 0;
+  __syncthreads();
+  const long long units = (long long)total_cost * p.n_hg;
+  const int t0 = (int)min((long long)kMaxBins,
+                          max((long long)kMinChunkTiles, (units + p.target_chunks - 1) / p.target_chunks));
+  if (p.split_slots > 0 && hist[tid] > 0) {
+    for (int ci = 0; ci < kCand; ++ci) {
+      const int t = t0 << ci;
+      if (tid > t) atomicAdd(&need[ci], min(hist[tid] * min((tid + t - 1) / t, 255), 1 << 24));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int t = INT_MAX;
+    if (p.split_slots > 0) {
+      for (int ci = kCand - 1; ci >= 0; --ci)
+        if (need[ci] <= p.split_slots) t = t0 << ci;
+    }
+    chunk_tiles = t;
+  }
+  __syncthreads();
+  const int T = chunk_tiles;
+  auto n_chunks = [&](int c) { return c > T ? min((c + T - 1) / T, 255) : 1; };
+  hist[tid] = 0;
+  __syncthreads();
+  for (int base = 0; base < n_items; base += kPlanThreads) {
+    const int idx = base + tid;
+    const int c = idx < n_items ? cost_of(idx) : -1;
+    const int nk = c < 0 ? 0 : n_chunks(c);
+    for (int k = 0; k < nk; ++k) atomicAdd(&hist[(k + 1) * c / nk - k * c / nk], 1);
+    wave_fetch_add(&count, nk);
   }
   __syncthreads();
   // Exclusive scan over bins in descending cost: start[c] = sum of hist[c'] for c' > c.
@@ -194,19 +286,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
   }
   hist[tid] = scan[buf][kMaxBins - 1 - tid];
   __syncthreads();
-  for (int idx = tid; idx < total; idx += kPlanThreads) {
+  for (int base = 0; base < n_items; base += kPlanThreads) {
+    const int idx = base + tid;
+    const int c = idx < n_items ? cost_of(idx) : -1;
+    const int nk = c < 0 ? 0 : n_chunks(c);
+    const int split_nk = nk > 1 ? nk : 0;
+    const int slot_at = wave_fetch_add(&slot_alloc, split_nk);
+    const int split_at = wave_fetch_add(&n_split, split_nk ? 1 : 0);
+    if (c < 0) continue;
     const int b = idx / p.n_qt_max, qt = idx - b * p.n_qt_max;
-    const Seq s = load_seq<PAGED>(p, b, causal != 0);
-    const int q_lo = qt * p.bm;
-    if (q_lo >= s.Lq) continue;
-    const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
-    const Tiles t = tile_range(s, i_lo, i_hi, p.g, causal != 0, bn);
-    const int cost = min(t.ta + t.tb1 - t.tb0, kMaxBins - 1);
-    const int pos = atomicAdd(&hist[cost], 1);
-    p.items[pos] = (b << 16) | qt;
+    int slot = 0xffff;
+    if (nk > 1) {
+      slot = slot_at;
+      p.split_items[2 * split_at] = (b << 16) | qt;
+      p.split_items[2 * split_at + 1] = (nk << 16) | slot;
+    }
+    for (int k = 0; k < nk; ++k) {
+      const int pos = atomicAdd(&hist[(k + 1) * c / nk - k * c / nk], 1);
+      p.items[2 * pos] = (b << 16) | qt;
+      p.items[2 * pos + 1] = (k << 24) | (nk << 16) | slot;
+    }
   }
+  __syncthreads();
   if (tid == 0) {
     *p.n_items = count;
+    *p.n_split = n_split;
     *p.counter = 0;
     *p.exited = 0;
   }
@@ -378,8 +482,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
   for (int w = next_item(&sh_item, p.counter); w < n_work; w = next_item(&sh_item, p.counter)) {
     const int item = w / p.n_hg;
     const int hg = w - item * p.n_hg;
-    const int packed = p.items[item];
+    const int packed = p.items[2 * item];
+    const int meta = p.items[2 * item + 1];
     const int b = packed >> 16, qt = packed & 0xffff;
+    const int chunk = (int)((uint32_t)meta >> 24), n_chunks = (meta >> 16) & 0xff, slot0 = meta & 0xffff;
     const Seq s = load_seq<PAGED>(p, b, CAUSAL);
     const int h = hg * hpw + (wave & (hpw - 1));
     const int rb = wave >> p.hpw_log2;
@@ -476,6 +582,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
     const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
     auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    // This chunk covers tiles [n_begin, n_end) of the item's tile sequence.
+    const int n_begin = chunk * n_tiles / n_chunks, n_end = (chunk + 1) * n_tiles / n_chunks;
 
     f32x16_t o[NDB];
 #pragma unroll
@@ -515,7 +623,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
             rv[jb][a] = x;
           }
       }
-      if (n + 1 < n_tiles) dma_tile(tile_at(n + 1), std::integral_constant<int, BUF ^ 1>{});
+      if (n + 1 < n_end) dma_tile(tile_at(n + 1), std::integral_constant<int, BUF ^ 1>{});
       if (!wave_active) return;
 
       const char* kbuf = kv_smem(bufc, 0);
@@ -677,14 +785,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
       }
     };
 
-    if (n_tiles > 0) dma_tile(tile_at(0), Buf0{});
-    for (int n = 0; n < n_tiles; n += 2) {
+    if (n_begin < n_end) dma_tile(tile_at(n_begin), Buf0{});
+    for (int n = n_begin; n < n_end; n += 2) {
       step(n, Buf0{});
-      if (n + 1 < n_tiles) step(n + 1, Buf1{});
+      if (n + 1 < n_end) step(n + 1, Buf1{});
     }
 
-    // Store: lane holds query l32, features d = 32 db + 8 a + 4 half + 0..3.
-    if (row_ok) {
+    // Lane holds query l32, features d = 32 db + 8 a + 4 half + 0..3.
+    if (n_chunks > 1) {
+      // Split item: store this chunk's fp32 partial; the reduction kernel
+      // sums the chunks in order (deterministic) and writes O.
+      if (row_ok) {
+        float* mine = p.partials + ((size_t)(slot0 + chunk) * p.n_hg + hg) * (kWaves * kRowsPerWave * D) +
+                      (size_t)(wave * kRowsPerWave + l32) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            f32x4_t y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = o[db][4 * a + e];
+            *(f32x4_t*)(mine + db * 32 + 8 * a + 4 * half) = y;
+          }
+      }
+    } else if (row_ok) {
       T* orow = (T*)p.out + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -698,6 +822,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     }
   }
   leave_queue(p);
+}
+
+// ------------------------------------------------------------------------
+// Split-K reduction: for each split item and head group, O = out_mul *
+// (partial of chunk 0 + chunk 1 + ...), summed in chunk order so the result
+// does not depend on which workgroup finished first.
+// ------------------------------------------------------------------------
+template <typename T, int D, bool PAGED>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p) {
+  constexpr int SLOT_FLOATS = kWaves * kRowsPerWave * D;
+  const int n_work = *p.n_split * p.n_hg;
+  const int hpw = 1 << p.hpw_log2;
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int it = w / p.n_hg, hg = w - it * p.n_hg;
+    const int packed = p.split_items[2 * it], meta = p.split_items[2 * it + 1];
+    const int b = packed >> 16, qt = packed & 0xffff;
+    const int nk = (meta >> 16) & 0xff, slot0 = meta & 0xffff;
+    const Seq s = load_seq<PAGED>(p, b, false);
+    const int q_lo = qt * p.bm;
+    const float* base = p.partials + ((size_t)slot0 * p.n_hg + hg) * SLOT_FLOATS;
+    const size_t chunk_stride = (size_t)p.n_hg * SLOT_FLOATS;
+    for (int f = threadIdx.x * 4; f < SLOT_FLOATS; f += kThreads * 4) {
+      const int wv = f / (kRowsPerWave * D);
+      const int row = (f / D) % kRowsPerWave;
+      const int d = f % D;
+      const int q_loc = q_lo + (wv >> p.hpw_log2) * kRowsPerWave + row;
+      if (q_loc >= s.Lq) continue;
+      const int h = hg * hpw + (wv & (hpw - 1));
+      f32x4_t acc = *(const f32x4_t*)(base + f);
+      for (int k = 1; k < nk; ++k) {
+        const f32x4_t x = *(const f32x4_t*)(base + k * chunk_stride + f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += x[e];
+      }
+      T y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (T)(acc[e] * p.out_mul);
+      *(u32x2_t*)((T*)p.out + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D + d) = *(const u32x2_t*)y;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -728,8 +892,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) v
   for (int w = next_item(&sh_item, p.counter); w < n_work; w = next_item(&sh_item, p.counter)) {
     const int item = w / p.n_hg;
     const int hg = w - item * p.n_hg;
-    const int packed = p.items[item];
+    const int packed = p.items[2 * item];
+    const int meta = p.items[2 * item + 1];
     const int b = packed >> 16, qt = packed & 0xffff;
+    const int chunk = (int)((uint32_t)meta >> 24), n_chunks = (meta >> 16) & 0xff, slot0 = meta & 0xffff;
     const Seq s = load_seq<PAGED>(p, b, CAUSAL);
     const int h = hg * hpw + (wave & (hpw - 1));
     const int rb = wave >> p.hpw_log2;
@@ -939,17 +1105,78 @@ KernelFn pick(DType dt, int D, bool causal, bool rab, int* bn, int* wpe) {
   return nullptr;
 }
 
+KernelFn pick_reduce(DType dt, int D, bool paged) {
+  switch (dt) {
+    case DType::BF16:
+      switch (D) {
+        case 32: return paged ? reduce_kernel<__bf16, 32, true> : reduce_kernel<__bf16, 32, false>;
+        case 64: return paged ? reduce_kernel<__bf16, 64, true> : reduce_kernel<__bf16, 64, false>;
+        case 128: return paged ? reduce_kernel<__bf16, 128, true> : reduce_kernel<__bf16, 128, false>;
+        case 256: return paged ? reduce_kernel<__bf16, 256, true> : reduce_kernel<__bf16, 256, false>;
+      }
+      break;
+    case DType::F16:
+      switch (D) {
+        case 32: return paged ? reduce_kernel<_Float16, 32, true> : reduce_kernel<_Float16, 32, false>;
+        case 64: return paged ? reduce_kernel<_Float16, 64, true> : reduce_kernel<_Float16, 64, false>;
+        case 128: return paged ? reduce_kernel<_Float16, 128, true> : reduce_kernel<_Float16, 128, false>;
+        case 256: return paged ? reduce_kernel<_Float16, 256, true> : reduce_kernel<_Float16, 256, false>;
+      }
+      break;
+    default:
+      break;
+  }
+  return nullptr;
+}
+
+// Workspace layout (all offsets 256-byte aligned):
+//   header: n_items, queue counter, exit counter
+//   work list: 2 ints per entry, at most items + split slots entries
+//   split counters: one int per (split slot, head group)
+//   partial sums: kWaves * 32 * head_dim floats per (split slot, head group)
+struct WsLayout {
+  size_t items, splits, partials, total;
+  int split_slots, n_qt_max, n_hg;
+};
+
+constexpr int kSplitUnits = 1024;  // (slot, head group) pairs of partial sums
+
+// Key-range splitting is used by the paged variant (few new-token queries
+// against long cached histories). For jagged batches the fixed cost of each
+// extra chunk (queue pop, sequence and Q loads, partial sums) outweighed the
+// shorter critical path on the measured workloads, so they are not split.
+bool use_split(int32_t batch, int n_qt_max, int n_hg, bool paged, DType dtype) {
+  if (dtype == DType::F32) return false;
+  (void)batch;
+  (void)n_qt_max;
+  (void)n_hg;
+  return paged;
+}
+
+WsLayout ws_layout(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                   DType dtype, bool paged) {
+  WsLayout w{};
+  const int group = num_heads_q / num_heads_kv;
+  const int hpw_log2 = heads_per_wg_log2(group);
+  const int bm = kRowsPerWave * (kWaves >> hpw_log2);
+  w.n_hg = num_heads_q >> hpw_log2;
+  w.n_qt_max = (max_q_len + bm - 1) / bm;
+  w.split_slots = use_split(batch, w.n_qt_max, w.n_hg, paged, dtype) ? max(2, kSplitUnits / w.n_hg) : 0;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t entries = (size_t)batch * w.n_qt_max + w.split_slots;
+  w.items = kHeaderBytes;
+  w.splits = up(w.items + entries * 2 * sizeof(int32_t));
+  w.partials = up(w.splits + (size_t)w.split_slots * 2 * sizeof(int32_t));
+  w.total = w.partials + (size_t)w.split_slots * w.n_hg * kWaves * kRowsPerWave * head_dim * sizeof(float);
+  return w;
+}
+
 }  // namespace
 
 size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, DType dtype) {
-  (void)head_dim;
-  (void)dtype;
-  if (batch < 0 || max_q_len < 0 || num_heads_q <= 0 || num_heads_kv <= 0) return 0;
-  const int group = num_heads_q / num_heads_kv;
-  const int bm = kRowsPerWave * (kWaves >> heads_per_wg_log2(group));
-  const size_t n_qt = ((size_t)max_q_len + bm - 1) / bm;
-  return kHeaderBytes + (size_t)batch * n_qt * sizeof(int32_t);
+                           int32_t head_dim, DType dtype, bool paged) {
+  if (batch < 0 || max_q_len < 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return 0;
+  return ws_layout(batch, max_q_len, num_heads_q, num_heads_kv, head_dim, dtype, paged).total;
 }
 
 namespace {
@@ -968,11 +1195,16 @@ KParams make_params(const FwdArgs& a) {
   p.page_offsets = a.page_offsets;
   p.page_ids = a.page_ids;
   p.last_page_len = a.last_page_len;
+  const WsLayout w = ws_layout(a.batch, a.max_seq_len, a.num_heads_q, a.num_heads_kv, a.head_dim, a.dtype, a.paged);
   char* ws = (char*)a.workspace;
   p.n_items = (int32_t*)ws;
   p.counter = (int32_t*)(ws + 64);
   p.exited = (int32_t*)(ws + 128);
-  p.items = (int32_t*)(ws + kHeaderBytes);
+  p.n_split = (int32_t*)(ws + 192);
+  p.items = (int32_t*)(ws + w.items);
+  p.split_items = (int32_t*)(ws + w.splits);
+  p.partials = (float*)(ws + w.partials);
+  p.split_slots = w.split_slots;
   p.batch = a.batch;
   p.max_seq_len = a.max_seq_len;
   p.Hq = a.num_heads_q;
@@ -981,7 +1213,7 @@ KParams make_params(const FwdArgs& a) {
   p.hpw_log2 = heads_per_wg_log2(p.group);
   p.n_hg = a.num_heads_q >> p.hpw_log2;
   p.bm = kRowsPerWave * (kWaves >> p.hpw_log2);
-  p.n_qt_max = (a.max_seq_len + p.bm - 1) / p.bm;
+  p.n_qt_max = w.n_qt_max;
   int ps_log2 = 0;
   while (a.paged && (1 << ps_log2) < a.page_size) ++ps_log2;
   p.ps_log2 = ps_log2;
@@ -993,6 +1225,8 @@ KParams make_params(const FwdArgs& a) {
   // multiplies by y = c s (Q pre-scaled) and folds -1/log2(e) instead.
   p.c_exp = -a.alpha * kLog2e;
   p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : -a.out_scale / kLog2e;
+  const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256 || a.paged;
+  p.target_chunks = num_cus() * (one_wave ? 1 : 2);
   return p;
 }
 
@@ -1016,11 +1250,18 @@ hipError_t launch_run(const FwdArgs& a) {
   KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, &bn, &wpe)
                         : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, &bn, &wpe);
   if (!fn) return hipErrorInvalidValue;
-  const long long upper = (long long)a.batch * p.n_qt_max * p.n_hg;
+  const long long upper = ((long long)a.batch * p.n_qt_max + p.split_slots) * p.n_hg;
   const long long cap = (long long)num_cus() * wpe;
   const int grid = (int)(upper < cap ? upper : cap);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, a.stream, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.split_slots == 0) return err;
+  KernelFn red = pick_reduce(a.dtype, a.head_dim, a.paged);
+  if (!red) return hipErrorInvalidValue;
+  const long long rupper = (long long)(p.split_slots / 2) * p.n_hg;
+  const long long rcap = (long long)num_cus() * 4;
+  hipLaunchKernelGGL(red, dim3((int)(rupper < rcap ? rupper : rcap)), dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 

@@ -179,7 +179,10 @@ def test_gqa_equals_repeated_mha_on_gpu(dev):
     vrep = c.v.repeat_interleave(4, dim=1).contiguous().to(dev)
     b = hj.hstu_fwd(c.q.to(dev), krep, vrep, torch.as_tensor(c.seq_offsets), num_targets=c.num_targets,
                     max_seq_len=c.max_seq_len, target_group_size=1, alpha=c.alpha, out_scale=c.out_scale)
-    assert torch.equal(a, b)
+    # The two layouts tile and split the key range differently, so fp32
+    # partial sums are grouped differently: equal up to output rounding.
+    d = (a.double() - b.double()).abs().max().item()
+    assert d <= 2e-3 * b.double().abs().max().item(), d
 
 
 @pytest.mark.parametrize("page_size", [32, 64, 128, 256])
