@@ -19,7 +19,6 @@ import argparse
 import json
 import math
 import os
-import statistics
 import sys
 import time
 
@@ -39,7 +38,48 @@ def parse():
     ap.add_argument("--workload", default="bf16_mha_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload (extra lines for analysis)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only plain 1 GiB device copies (the reference point for the HBM byte counters)")
     return ap.parse_args()
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "hstu_jagged_attention_amd", "csrc", "hstu_kernels.hip")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_sha256():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of the forward kernel on this workload, as read
+    by the FETCH_SIZE and WRITE_SIZE counters and scaled by what the same
+    counters read for a plain copy of known size. The record names the
+    sha256 of the kernel source it was taken on; a record taken on other
+    source gives None (the figure no longer describes the kernel)."""
+    path = os.path.join(ROOT, "profiles", f"fwd_kernel_{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(dev):
+    """Plain device-to-device copies of COPY_BYTES each (read COPY_BYTES, write
+    COPY_BYTES): the reference kernel for scaling the byte counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 5}), flush=True)
 
 
 def build_step(name, dev):
@@ -121,14 +161,15 @@ def cpu_baseline(c, name, flops_full):
                                       target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale,
                                       rows=rows)
         sample, fl = "every 16th query row of every sequence, all heads", 4.0 * c.head_dim * pairs
-    times = []
-    for _ in range(3):
+    # Repeat the sample until about 10 s of CPU work has been timed.
+    runs, total = 0, 0.0
+    while runs == 0 or total < 10.0:
         t0 = time.perf_counter()
         run()
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{sample}; median of 3 runs, {t:.3f} s each"}
+        total += time.perf_counter() - t0
+        runs += 1
+    return {"value": fl * runs / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}; {runs} runs in {total:.2f} s"}
 
 
 def measure(name, args, dev):
@@ -147,26 +188,31 @@ def measure(name, args, dev):
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # Per-kernel launch durations with HIP events on the launch stream.
+    # Per-kernel launch durations with HIP events on the launch stream: K
+    # back-to-back launches of one phase between two events, so the event
+    # markers' own latency is amortised over K launches (a plan stays valid
+    # for any number of runs: the run kernel rewinds its queue counters).
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / n
+
     n_ev = max(args.steps, 10)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-    for e in ev:
-        e[0].record(stream)
-        prep.plan()
-        e[1].record(stream)
-        prep.run()
-        e[2].record(stream)
-    torch.cuda.synchronize(dev)
-    plan_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
-    run_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in ev)
-    run_ms_median = statistics.median(e[1].elapsed_time(e[2]) for e in ev)
+    plan_ms = timed(prep.plan, n_ev)
+    prep.plan()
+    run_ms = timed(prep.run, n_ev)
     achieved_tflops = flops / (run_ms * 1e-3) / 1e12
     dtype = c.dtype
     peak = PEAK_TFLOPS[dtype]
     hbm_gbs = alg_bytes / (run_ms * 1e-3) / 1e9
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved_tflops / peak, 4), "traffic": None,
-                "kernel": "fwd_kernel", "launch_ms_mean": round(run_ms, 5), "launch_ms_median": round(run_ms_median, 5),
+                "frac": round(achieved_tflops / peak, 4), "traffic": measured_traffic(name),
+                "kernel": "fwd_kernel" + ("+reduce_kernel" if name == "bf16_paged_target" else ""),
+                "launch_ms_mean": round(run_ms, 5),
                 "plan_kernel_ms_mean": round(plan_ms, 5), "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
                 "algorithmic_hbm_GBps": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -194,6 +240,9 @@ def main():
     import hstu_jagged_attention_amd as hj
     hj.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
     names = ["tiny_fp32_bidirectional", "bf16_mha_causal", "bf16_rab_target", "fp16_gqa_causal",
              "bf16_paged_target"] if args.all else [args.workload]
     for name in names:
