@@ -48,9 +48,13 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_source_sha256():
+    """sha256 of the kernel source with // comments and blank lines removed
+    (a comment edit does not change the kernel the counters describe)."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(KERNEL_SOURCE) as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
 def measured_traffic(name):

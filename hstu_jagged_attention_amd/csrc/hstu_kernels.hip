@@ -8,7 +8,7 @@
 // variant whose history K/V live in kv_cache pages. No softmax: partial sums
 // over key tiles add exactly, so no running max or rescale is kept.
 //
-// Two kernels per call, both on the caller's stream:
+// Kernels per call, all on the caller's stream:
 //  1. plan_kernel: one workgroup turns seq_offsets (and the mask inputs)
 //     into the work list: one item per (sequence, query tile), costed by the
 //     number of key tiles that are not fully masked, counting-sorted longest
@@ -17,12 +17,17 @@
 //     in list order. A workgroup owns one item and a group of query heads
 //     that share one kv head (1 head x 128 rows for MHA, up to 4 heads x 32
 //     rows for GQA), so each K/V tile is staged through LDS once for all of
-//     them. Per key tile: S^T = K Q^T on MFMA (the accumulator then holds
-//     one query per lane and 16 keys per lane), the SiLU epilogue in
-//     registers, then O^T += V^T P^T on MFMA with P used straight from the
-//     S^T registers as the B operand. The key order inside a 32-key block is
-//     permuted (bits 2 and 3 swapped) when V^T is written to LDS, so both
-//     MFMA operands of the second product read 16 contiguous bytes per lane.
+//     them. K/V tiles go global -> LDS by DMA (no register staging), double
+//     buffered, rows stored as 16-byte chunks under an XOR swizzle. Per key
+//     tile: S^T = K Q^T on MFMA (the accumulator then holds one query per
+//     lane and 16 keys per lane), the SiLU epilogue in registers, then
+//     O^T += V^T P^T on MFMA with P used straight from the S^T registers as
+//     the B operand; the V^T A operand comes from transposing LDS reads of
+//     the row-major V tile, taken in the key order the S^T accumulator
+//     holds (bits 2 and 3 of the key index inside a 32-key block swapped).
+//  3. reduce_kernel (paged calls with split items only): items longer than
+//     the planner's chunk size run as several key-range chunks that store
+//     fp32 partial O; this kernel sums them in chunk order.
 //
 // MFMA lane layouts (checked on the device): v_mfma_f32_32x32x16_{bf16,f16}
 // takes A[m = lane%32][k = 8*(lane/32) + 0..7] and B[k = 8*(lane/32) + 0..7]
