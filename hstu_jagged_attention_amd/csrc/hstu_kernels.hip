@@ -356,8 +356,11 @@ __device__ inline const T* kv_row(const KParams& p, const Seq& s, int hk, int j,
   return (const T*)(which ? p.v : p.k) + ((size_t)(s.k_tok0 + j) * p.Hk + hk) * D;
 }
 
-// Position of key k (0 <= k < tile) in a V^T row: bits 2 and 3 swapped.
-__device__ inline int vt_pos(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Bits [0, n) set, n clamped to [0, 32].
+__device__ inline uint32_t low_bits(int n) {
+  n = min(max(n, 0), 32);
+  return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+}
 
 __device__ inline int next_item(int* sh, int* counter) {
   __syncthreads();
@@ -371,7 +374,8 @@ __device__ inline int next_item(int* sh, int* counter) {
 // that one can rewind the queue for the next run of the same plan.
 __device__ inline void leave_queue(const KParams& p) {
   if (threadIdx.x == 0) {
-    __threadfence();
+    // The workgroup's last pop returned before this point (its value ended
+    // the loop), so it is ordered before this count without a fence.
     const int done = atomicAdd(p.exited, 1);
     if (done == (int)gridDim.x - 1) {
       atomicExch(p.counter, 0);
@@ -462,7 +466,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     constexpr int B = decltype(bufc)::value;
     if constexpr (B == 0) return which ? smem_v0 : smem_k0; else return which ? smem_v1 : smem_k1;
   };
-  __shared__ int sh_item;
+  __shared__ int sh_item[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -484,7 +488,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
   for (int u = 0; u < KB_PER_WAVE; ++u) dma_off_b[u] = (uint32_t)dma_row(u) * row_stride_b + dma_col_b(u);
 
-  for (int w = next_item(&sh_item, p.counter); w < n_work; w = next_item(&sh_item, p.counter)) {
+  // Work item w of workgroup g: first w = g, then, when there are more
+  // items than workgroups, gridDim.x + (pops of the shared counter). The
+  // pop for the next item is issued when an item starts, so its latency
+  // hides behind the item's first tile load.
+  const bool dyn = (int)gridDim.x < n_work;
+  int w = blockIdx.x, parity = 0;
+  while (w < n_work) {
+    int w_next = n_work;
+    if (dyn && tid == 0) w_next = (int)gridDim.x + atomicAdd(p.counter, 1);
     const int item = w / p.n_hg;
     const int hg = w - item * p.n_hg;
     const int packed = p.items[2 * item];
@@ -662,14 +674,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
         return __builtin_bit_cast(V8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
       };
 
-      // Mask bounds relative to the lane's first key of block jb.
-      int ma[NJB], mb[NJB], mc[NJB];
+      // Visibility of the lane's keys in block jb as a bit mask over the
+      // offset from its first key j = j0 + 32 jb + 4 half: bit o is set iff
+      // key j + o is visible, i.e. o <= a_i - j or b_i - j <= o <= i - j.
+      uint32_t vis[NJB];
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const int jbase = j0 + jb * 32 + 4 * half;
-        ma[jb] = a_i - jbase;
-        mb[jb] = b_i == INT_MAX ? INT_MAX / 2 : b_i - jbase;
-        mc[jb] = i - jbase;
+        const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
+        vis[jb] = low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg));
       }
       f32x16_t sacc[NJB];
       V8 pf[NJB][2];
@@ -688,15 +701,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
           y = __builtin_fmaf(rab_f, p.c_exp, y);
         }
         if constexpr (decltype(masked)::value) {
-          // Masked keys get y = +0 (bitwise AND), hence p = 0 * 1/2 = 0
-          // exactly, and a NaN rab there never reaches the arithmetic. Both
-          // variants run the same arithmetic otherwise, so results do not
-          // depend on which tiles a configuration classifies as full. With
-          // off = key offset inside the lane's 32-key block, key j is
-          // visible iff max(a_i - j, min(j - b_i, i - j)) >= 0.
+          // Masked keys get y = +0 (bitwise AND with the sign-extended
+          // visibility bit), hence p = 0 * 1/2 = 0 exactly, and a NaN rab
+          // there never reaches the arithmetic. Both variants run the same
+          // arithmetic otherwise, so results do not depend on which tiles a
+          // configuration classifies as full.
           const int off = 8 * (r / 4) + (r % 4);  // unrolled: a constant
-          const int v = max(ma[jb] - off, min(off - mb[jb], mc[jb] - off));
-          y = __builtin_bit_cast(float, __builtin_bit_cast(int, y) & ~(v >> 31));
+          const int keep = (int)(vis[jb] << (31 - off)) >> 31;
+          y = __builtin_bit_cast(float, __builtin_bit_cast(int, y) & keep);
         }
         const float e = __builtin_amdgcn_exp2f(y);
         const float pv = y * __builtin_amdgcn_rcpf(1.f + e);
@@ -813,8 +825,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
             *(f32x4_t*)(mine + db * 32 + 8 * a + 4 * half) = y;
           }
       }
-    } else if (row_ok) {
-      T* orow = (T*)p.out + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D;
+    } else {
+      // Stage the wave's 32 x D output rows through LDS (its own buffer:
+      // every K/V buffer is free once all waves pass the barrier) and write
+      // them back as whole rows, 16 bytes per lane.
+      __syncthreads();
+      char* stg = wave == 0 ? smem_k0 : wave == 1 ? smem_v0 : wave == 2 ? smem_k1 : smem_v1;
+      // The lane index is re-read here so that the address arithmetic below
+      // is not hoisted out of the item loop (it would hold registers there).
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int r32 = ln & 31, hf = ln >> 5;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -822,11 +843,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
           T y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = (T)(o[db][4 * a + e] * p.out_mul);
-          *(u32x2_t*)(orow + db * 32 + 8 * a + 4 * half) = *(const u32x2_t*)y;
+          const int f0 = db * 32 + 8 * a + 4 * hf;
+          *(u32x2_t*)(stg + r32 * ROW_B + (((f0 >> 3) ^ swz<D>(r32)) * 16) + (f0 & 7) * 2) = *(const u32x2_t*)y;
         }
+      __builtin_amdgcn_wave_barrier();
+      constexpr int CPR = D / 8;  // 16-byte chunks per output row
+      const int row0 = q_lo + rb * kRowsPerWave;
+#pragma unroll
+      for (int it = 0; it < kRowsPerWave * CPR / 64; ++it) {
+        const int idx = it * 64 + ln, row = idx / CPR, c = idx % CPR;
+        const u32x4_t x = *(const u32x4_t*)(stg + row * ROW_B + ((c ^ swz<D>(row)) * 16));
+        if (row0 + row < s.Lq) *(u32x4_t*)((T*)p.out + ((size_t)(s.q_tok0 + row0 + row) * p.Hq + h) * D + c * 8) = x;
+      }
     }
+    if (tid == 0) sh_item[parity] = w_next;
+    __syncthreads();
+    w = __builtin_amdgcn_readfirstlane(sh_item[parity]);  // uniform: keeps item state in SGPRs
+    parity ^= 1;
   }
-  leave_queue(p);
+  if (dyn) leave_queue(p);
 }
 
 // ------------------------------------------------------------------------
@@ -1064,7 +1099,7 @@ using KernelFn = void (*)(KParams);
 template <typename T, int D, bool PAGED>
 KernelFn pick16(bool causal, bool rab) {
   constexpr int BN = D >= 256 ? 32 : 64;
-  constexpr int WPE = PAGED ? 1 : (D >= 256 ? 1 : 2);
+  constexpr int WPE = D >= 256 ? 1 : 2;
   if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE> : fwd_kernel<T, D, BN, false, false, true, WPE>;
   if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE> : fwd_kernel<T, D, BN, true, false, false, WPE>;
   return rab ? fwd_kernel<T, D, BN, false, true, false, WPE> : fwd_kernel<T, D, BN, false, false, false, WPE>;
@@ -1081,7 +1116,7 @@ KernelFn pick32(bool causal, bool rab) {
 template <bool PAGED>
 KernelFn pick(DType dt, int D, bool causal, bool rab, int* bn, int* wpe) {
   *bn = (dt != DType::F32 && D >= 256) ? 32 : 64;
-  *wpe = (dt == DType::F32 || D >= 256 || PAGED) ? 1 : 2;
+  *wpe = (dt == DType::F32 || D >= 256) ? 1 : 2;
   switch (dt) {
     case DType::BF16:
       switch (D) {
@@ -1230,7 +1265,7 @@ KParams make_params(const FwdArgs& a) {
   // multiplies by y = c s (Q pre-scaled) and folds -1/log2(e) instead.
   p.c_exp = -a.alpha * kLog2e;
   p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : -a.out_scale / kLog2e;
-  const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256 || a.paged;
+  const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256;
   p.target_chunks = num_cus() * (one_wave ? 1 : 2);
   return p;
 }
