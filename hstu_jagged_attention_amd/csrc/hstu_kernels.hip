@@ -90,6 +90,8 @@ struct KParams {
   int32_t n_hg;       // Hq >> hpw_log2
   int32_t bm;         // query rows per item = 32 * (4 >> hpw_log2)
   int32_t n_qt_max;   // q tiles per sequence, upper bound
+  int32_t direct_items; // > 0: no work list; workgroup w runs item w of the
+                        // full (sequence, q tile, head group) grid
   int32_t ps_log2;    // log2(page_size)
   int32_t g;          // target_group_size
   int32_t rab_vec;    // rab rows allow 4-element vector loads
@@ -421,10 +423,26 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the
-// wave writes lds_base + 16 l (lds_base must be wave-uniform).
+// wave writes lds_base + 16 l (lds_base must be wave-uniform; it goes in M0).
+// Written as inline assembly on purpose: the compiler then does not track
+// these LDS writes, so it does not make reads of the other buffer wait for
+// the prefetch in flight (its alias analysis cannot always separate them).
+// The kernel orders them itself: a vmcnt(0) wait and a barrier before any
+// wave reads a filled buffer, and a barrier between the last read of a
+// buffer and the next DMA into it. The DMA reads M0 one cycle after it
+// issues, so a wait state separates it from the M0 write the compiler
+// places right before the statement (the compiler adds the same s_nop to
+// its own LDS DMA; it cannot see into this one).
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)p;
+}
+// The source address is a per-lane 64-bit VGPR pair (the form the compiler
+// itself uses after a VALU address add). No SGPR operand: a VMEM read of an
+// SGPR written by a VALU instruction (v_readfirstlane) needs five wait
+// states, which the compiler cannot insert for an asm statement.
 __device__ inline void dma16(const void* src, void* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_addr(lds_base)));
 #endif
 }
 
@@ -440,70 +458,113 @@ __device__ inline v4i16_t lds_read_tr16(const void* addr) {
 
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void fwd_kernel(KParams p) {
+// KSP = 1: a workgroup of 4 waves walks all key tiles of its item.
+// KSP = 2: 8 waves in two groups of 4; group g takes key tiles g, g+2, ...
+// of the item (each group with its own LDS buffers) and the two partial
+// O tiles are summed through LDS at the end. This halves an item's latency,
+// for work lists too short to fill the chip.
+template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE, int KSP>
+__global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(WPE))) void fwd_kernel(KParams p) {
   using F = Frag<T>;
   using V8 = typename F::v8;
   constexpr int KS = D / 16;    // k steps of S^T = K Q^T
   constexpr int NJB = BN / 32;  // 32-key blocks per tile
   constexpr int NDB = D / 32;   // 32-wide blocks of O^T
-  constexpr int ROW_B = D * 2;  // bytes per key row
-  constexpr int TILE_B = BN * ROW_B;
-  constexpr int KB_PER_TILE = TILE_B / 1024;  // 1 KB DMA blocks per tile
-  constexpr int KB_PER_WAVE = (KB_PER_TILE + kWaves - 1) / kWaves;
-  static_assert(TILE_B % 1024 == 0, "tile must be a whole number of 1 KB DMA blocks");
+  constexpr int ROW_B = D * 2;  // bytes per key row in global memory
+  // LDS rows are padded so that every fragment read is bank-conflict free
+  // with plain (unswizzled) addresses, i.e. one base register per lane and
+  // compile-time offsets: a K row is followed by 16 bytes (16 consecutive
+  // rows then start in 16 different 4-bank groups); a V row stride is 64
+  // bytes past a multiple of 256 (the 4 rows x 64 bytes a half-wave
+  // transposing read touches then cover all 64 banks once).
+  constexpr int KS_B = ROW_B + 16;
+  constexpr int VS_B = ROW_B + (ROW_B % 256 == 64 ? 0 : 64);
+  constexpr int K_SLOTS = KS_B / 16, V_SLOTS = VS_B / 16;  // 16-byte slots per LDS row
+  constexpr int K_TILE_B = (BN * KS_B + 1023) / 1024 * 1024;  // whole 1 KB DMA blocks
+  constexpr int V_TILE_B = (BN * VS_B + 1023) / 1024 * 1024;
+  constexpr int K_BLK = K_TILE_B / 1024, V_BLK = V_TILE_B / 1024;
+  constexpr int K_BLK_W = (K_BLK + kWaves - 1) / kWaves, V_BLK_W = (V_BLK + kWaves - 1) / kWaves;
+  static_assert(KSP == 1 || (KSP == 2 && BN == 64), "the key split exchanges O through one 64-key K/V buffer per wave");
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
 
   // Separate objects per buffer: the compiler's alias analysis can then see
   // that the DMA filling one buffer does not write the one being read, and
   // does not wait for the prefetch before reading the current tile.
-  __shared__ __attribute__((aligned(1024))) char smem_k0[TILE_B];
-  __shared__ __attribute__((aligned(1024))) char smem_v0[TILE_B];
-  __shared__ __attribute__((aligned(1024))) char smem_k1[TILE_B];
-  __shared__ __attribute__((aligned(1024))) char smem_v1[TILE_B];
-  auto kv_smem = [&](auto bufc, int which) -> char* {
-    constexpr int B = decltype(bufc)::value;
-    if constexpr (B == 0) return which ? smem_v0 : smem_k0; else return which ? smem_v1 : smem_k1;
-  };
+  // One slice per key group; group g uses slice g of every array.
+  __shared__ __attribute__((aligned(1024))) char smem_k0[KSP][K_TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_v0[KSP][V_TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_k1[KSP][K_TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_v1[KSP][V_TILE_B];
   __shared__ int sh_item[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wave_id & (kWaves - 1);  // role inside the key group
   const int l32 = lane & 31, half = lane >> 5;
-  const int n_work = *p.n_items * p.n_hg;
+  const bool direct = p.direct_items > 0;
+  const int n_work = direct ? p.direct_items : *p.n_items * p.n_hg;
   const int hpw = 1 << p.hpw_log2;
   const uint32_t row_stride_b = (uint32_t)p.Hk * ROW_B;  // bytes between key rows of one kv head
 
-  // DMA geometry of this lane, the same for every tile: lane `lane` of
-  // block `blk` fills LDS byte o = blk*1024 + lane*16 of a tile, i.e. row
-  // o / ROW_B and chunk slot (o % ROW_B) / 16, which holds global chunk
-  // slot ^ swz(row).
-  auto dma_row = [&](int u) { return ((wave * KB_PER_WAVE + u) * 1024 + lane * 16) / ROW_B; };
-  auto dma_col_b = [&](int u) {
-    const int o = (wave * KB_PER_WAVE + u) * 1024 + lane * 16;
-    return (uint32_t)((((o % ROW_B) / 16) ^ swz<D>(o / ROW_B)) * 16);
+  // DMA geometry of this lane, the same for every tile: lane `lane` of the
+  // wave's block u fills 16-byte LDS slot (blk * 64 + lane) of a tile, with
+  // blk = wave + kWaves u, i.e. row slot / SLOTS and chunk slot % SLOTS.
+  // Padding slots, and slots past the last row, load chunk 0 of a valid row
+  // (the bytes are never read).
+  auto slot_row = [&](int slots, int blk) { return min((blk * 64 + lane) / slots, BN - 1); };
+  auto slot_col_b = [&](int slots, int blk) {
+    const int c = (blk * 64 + lane) % slots;
+    return (uint32_t)(c < ROW_B / 16 && (blk * 64 + lane) / slots < BN ? c * 16 : 0);
   };
-  uint32_t dma_off_b[KB_PER_WAVE];
+  uint32_t dma_k_off[K_BLK_W], dma_v_off[V_BLK_W];
 #pragma unroll
-  for (int u = 0; u < KB_PER_WAVE; ++u) dma_off_b[u] = (uint32_t)dma_row(u) * row_stride_b + dma_col_b(u);
+  for (int u = 0; u < K_BLK_W; ++u) {
+    const int blk = wave + kWaves * u;
+    dma_k_off[u] = (uint32_t)slot_row(K_SLOTS, blk) * row_stride_b + slot_col_b(K_SLOTS, blk);
+  }
+#pragma unroll
+  for (int u = 0; u < V_BLK_W; ++u) {
+    const int blk = wave + kWaves * u;
+    dma_v_off[u] = (uint32_t)slot_row(V_SLOTS, blk) * row_stride_b + slot_col_b(V_SLOTS, blk);
+  }
 
+  // Each key group runs its own copy of the loop with its group index as a
+  // constant, so every LDS buffer address is known at compile time (which
+  // lets the compiler see that a DMA into one buffer never aliases reads of
+  // another). Both copies execute the same sequence of barriers.
+  const bool dyn = (int)gridDim.x < n_work;
+  auto run = [&](auto grpc) {
+    constexpr int GRP = decltype(grpc)::value;
+    auto kv_smem = [&](auto bufc, int which) -> char* {
+      constexpr int B = decltype(bufc)::value;
+      if constexpr (B == 0) return which ? smem_v0[GRP] : smem_k0[GRP]; else return which ? smem_v1[GRP] : smem_k1[GRP];
+    };
   // Work item w of workgroup g: first w = g, then, when there are more
   // items than workgroups, gridDim.x + (pops of the shared counter). The
   // pop for the next item is issued when an item starts, so its latency
   // hides behind the item's first tile load.
-  const bool dyn = (int)gridDim.x < n_work;
   int w = blockIdx.x, parity = 0;
   while (w < n_work) {
     int w_next = n_work;
     if (dyn && tid == 0) w_next = (int)gridDim.x + atomicAdd(p.counter, 1);
     const int item = w / p.n_hg;
     const int hg = w - item * p.n_hg;
-    const int packed = p.items[2 * item];
-    const int meta = p.items[2 * item + 1];
-    const int b = packed >> 16, qt = packed & 0xffff;
+    int b, qt, meta = (1 << 16);  // direct items: one chunk
+    if (direct) {
+      b = item / p.n_qt_max;
+      qt = item - b * p.n_qt_max;
+    } else {
+      const int packed = p.items[2 * item];
+      meta = p.items[2 * item + 1];
+      b = packed >> 16;
+      qt = packed & 0xffff;
+    }
     const int chunk = (int)((uint32_t)meta >> 24), n_chunks = (meta >> 16) & 0xff, slot0 = meta & 0xffff;
     const Seq s = load_seq<PAGED>(p, b, CAUSAL);
+    // A direct item past the end of its sequence has no rows; in direct mode
+    // every workgroup has exactly one item, so it simply has no work.
+    if (direct && qt * p.bm >= s.Lq) break;
     const int h = hg * hpw + (wave & (hpw - 1));
     const int rb = wave >> p.hpw_log2;
     const int hk = (hg * hpw) / p.group;
@@ -553,27 +614,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
       const char *kb, *vb;
       if (tile_bases(j0, kb, vb)) {
 #pragma unroll
-        for (int u = 0; u < KB_PER_WAVE; ++u) {
-          const int blk = wave * KB_PER_WAVE + u;
-          if (KB_PER_TILE % kWaves == 0 || blk < KB_PER_TILE) {
-            dma16(kb + dma_off_b[u], kv_smem(bufc, 0) + blk * 1024);
-            dma16(vb + dma_off_b[u], kv_smem(bufc, 1) + blk * 1024);
-          }
+        for (int u = 0; u < K_BLK_W; ++u) {
+          const int blk = wave + kWaves * u;
+          if (K_BLK % kWaves == 0 || blk < K_BLK) dma16(kb + dma_k_off[u], kv_smem(bufc, 0) + blk * 1024);
+        }
+#pragma unroll
+        for (int u = 0; u < V_BLK_W; ++u) {
+          const int blk = wave + kWaves * u;
+          if (V_BLK % kWaves == 0 || blk < V_BLK) dma16(vb + dma_v_off[u], kv_smem(bufc, 1) + blk * 1024);
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < KB_PER_WAVE; ++u) {
-          const int blk = wave * KB_PER_WAVE + u;
-          if (KB_PER_TILE % kWaves == 0 || blk < KB_PER_TILE) {
-            const int j = min(j0 + dma_row(u), s.L - 1);
-            const char* krow = (const char*)kv_row<T, D, PAGED>(p, s, hk, j, 0) + dma_col_b(u);
-            const char* vrow = (const char*)kv_row<T, D, PAGED>(p, s, hk, j, 1) + dma_col_b(u);
-            dma16(krow, kv_smem(bufc, 0) + blk * 1024);
-            dma16(vrow, kv_smem(bufc, 1) + blk * 1024);
+        for (int u = 0; u < K_BLK_W; ++u) {
+          const int blk = wave + kWaves * u;
+          if (K_BLK % kWaves == 0 || blk < K_BLK) {
+            const int j = min(j0 + slot_row(K_SLOTS, blk), s.L - 1);
+            dma16((const char*)kv_row<T, D, PAGED>(p, s, hk, j, 0) + slot_col_b(K_SLOTS, blk), kv_smem(bufc, 0) + blk * 1024);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < V_BLK_W; ++u) {
+          const int blk = wave + kWaves * u;
+          if (V_BLK % kWaves == 0 || blk < V_BLK) {
+            const int j = min(j0 + slot_row(V_SLOTS, blk), s.L - 1);
+            dma16((const char*)kv_row<T, D, PAGED>(p, s, hk, j, 1) + slot_col_b(V_SLOTS, blk), kv_smem(bufc, 1) + blk * 1024);
           }
         }
       }
     };
+
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
+    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
+    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    // This chunk covers tiles [n_begin, n_end) of the item's tile sequence.
+    const int n_begin = chunk * n_tiles / n_chunks, n_end = (chunk + 1) * n_tiles / n_chunks;
+    const int n_steps = (n_end - n_begin + KSP - 1) / KSP;
+    // The first tile's DMA goes out before the Q load, to overlap their latencies.
+    if (n_begin + GRP < n_end) dma_tile(tile_at(n_begin + GRP), Buf0{});
 
     // Q fragments (B operand of S^T = K Q^T), pre-scaled by c.
     V8 qf[KS];
@@ -596,11 +673,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     const int a_i = CAUSAL ? min(hi_i, s.H - 1) : s.L - 1;
     const int b_i = CAUSAL ? max(tlo_i, s.H) : INT_MAX;
 
-    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
-    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
-    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
-    // This chunk covers tiles [n_begin, n_end) of the item's tile sequence.
-    const int n_begin = chunk * n_tiles / n_chunks, n_end = (chunk + 1) * n_tiles / n_chunks;
 
     f32x16_t o[NDB];
 #pragma unroll
@@ -613,9 +685,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
 
     // One key tile: publish its LDS buffer, request the next tile into the
     // other buffer, then S^T, epilogue and O^T on this one.
-    auto step = [&](int n, auto bufc) {
+    auto step = [&](int t, auto bufc) {
       constexpr int BUF = decltype(bufc)::value;
-      const int kt = tile_at(n);
+      const int n = n_begin + KSP * t + GRP;
+      const bool has_tile = n < n_end;
+      const int kt = tile_at(has_tile ? n : n_begin);
       wait_vmem_all();
       __syncthreads();
       const int j0 = kt * BN;
@@ -640,8 +714,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
             rv[jb][a] = x;
           }
       }
-      if (n + 1 < n_end) dma_tile(tile_at(n + 1), std::integral_constant<int, BUF ^ 1>{});
-      if (!wave_active) return;
+      if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
+      if (!wave_active || !has_tile) return;
 
       const char* kbuf = kv_smem(bufc, 0);
       const char* vbuf = kv_smem(bufc, 1);
@@ -656,7 +730,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
       // K fragment (A operand of S^T) for key block jb, k step ks.
       auto k_frag = [&](int jb, int ks) -> V8 {
         const int row = jb * 32 + l32;
-        return *(const V8*)(kbuf + row * ROW_B + (((2 * ks + half) ^ swz<D>(row)) * 16));
+        return *(const V8*)(kbuf + row * KS_B + (2 * ks + half) * 16);
       };
       // V^T fragment (A operand of O^T += V^T P^T) for (jb, m, db): two
       // transposing reads; the 16-lane group G = lane/16 reads key rows
@@ -669,7 +743,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
         for (int u = 0; u < 2; ++u) {
           const int row = jb * 32 + 16 * m + 8 * u + 4 * (G >> 1) + (sl >> 2);
           const int col = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-          part[u] = lds_read_tr16(vbuf + row * ROW_B + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2);
+          part[u] = lds_read_tr16(vbuf + row * VS_B + col * 2);
         }
         return __builtin_bit_cast(V8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
       };
@@ -774,18 +848,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
         // Two waves per SIMD: keep the register footprint small and let the
         // other workgroup on the SIMD fill the gaps; only the epilogue
         // differs between full and masked tiles.
+        // S^T: the key blocks alternate, so consecutive MFMAs are
+        // independent; K fragments are read PF_S MFMAs ahead.
+        constexpr int NS = KS * NJB, PF_S = 4;
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
+        for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) sacc[jb] = F::mfma(k_frag(jb, ks), qf[ks], sacc[jb]);
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) sacc[jb] = F::mfma(k_frag(jb, ks), qf[ks], sacc[jb]);
+        __builtin_amdgcn_sched_group_barrier(0x100, PF_S, 1);  // DS reads
+#pragma unroll
+        for (int q = 0; q < NS - PF_S; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF_S, 1);
         auto epi_all = [&](auto masked) {
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) epi(masked, jb, r);
+          if constexpr (!decltype(masked)::value && !RAB) {
+            // Keep eight elements in flight (exp, add, rcp, mul per element,
+            // one packed convert per two): without this the scheduler
+            // chains the elements one after another through one register.
+#pragma unroll
+            for (int g8 = 0; g8 < NJB * 2; ++g8) {
+              __builtin_amdgcn_sched_group_barrier(0x400, 8, 0);  // 8 exp
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // 8 add
+              __builtin_amdgcn_sched_group_barrier(0x400, 8, 0);  // 8 rcp
+              __builtin_amdgcn_sched_group_barrier(0x002, 12, 0); // 8 mul, 4 cvt
+            }
+          }
         };
         __builtin_amdgcn_sched_barrier(0);
         if (full)
@@ -793,23 +890,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
         else
           epi_all(std::true_type{});
         __builtin_amdgcn_sched_barrier(0);
+        // O^T: V^T fragments (two transposing reads each) PF_V MFMAs ahead.
+        constexpr int NP = NJB * 2 * NDB, PF_V = 4;
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] = F::mfma(v_frag(jb, m, db), pf[jb][m], o[db]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF_V, 2);
+#pragma unroll
+        for (int q = 0; q < NP - PF_V; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF_V, 2);
       }
     };
 
-    if (n_begin < n_end) dma_tile(tile_at(n_begin), Buf0{});
-    for (int n = n_begin; n < n_end; n += 2) {
-      step(n, Buf0{});
-      if (n + 1 < n_end) step(n + 1, Buf1{});
+    // Step t of group g works on tile n_begin + KSP t + g; every group runs
+    // the same number of steps (and barriers).
+    for (int t = 0; t < n_steps; t += 2) {
+      step(t, Buf0{});
+      if (t + 1 < n_steps) step(t + 1, Buf1{});
     }
 
+    // Every wave is done with the K/V buffers past this barrier; they serve
+    // as exchange and staging space below.
+    __syncthreads();
+    if constexpr (KSP > 1) {
+      // Group 1 hands its partial O^T to group 0 (same lane, same register).
+      char* xch = wave == 0 ? smem_k0[KSP - 1] : wave == 1 ? smem_v0[KSP - 1] : wave == 2 ? smem_k1[KSP - 1] : smem_v1[KSP - 1];
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      if (GRP == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            f32x4_t y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = o[db][4 * a + e];
+            *(f32x4_t*)(xch + ((db * 4 + a) * 64 + ln) * 16) = y;
+          }
+      }
+      __syncthreads();
+      if (GRP == 0) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4_t y = *(const f32x4_t*)(xch + ((db * 4 + a) * 64 + ln) * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[db][4 * a + e] += y[e];
+          }
+      }
+    }
     // Lane holds query l32, features d = 32 db + 8 a + 4 half + 0..3.
-    if (n_chunks > 1) {
+    if (GRP == 0 && n_chunks > 1) {
       // Split item: store this chunk's fp32 partial; the reduction kernel
       // sums the chunks in order (deterministic) and writes O.
       if (row_ok) {
@@ -825,12 +963,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
             *(f32x4_t*)(mine + db * 32 + 8 * a + 4 * half) = y;
           }
       }
-    } else {
-      // Stage the wave's 32 x D output rows through LDS (its own buffer:
-      // every K/V buffer is free once all waves pass the barrier) and write
-      // them back as whole rows, 16 bytes per lane.
-      __syncthreads();
-      char* stg = wave == 0 ? smem_k0 : wave == 1 ? smem_v0 : wave == 2 ? smem_k1 : smem_v1;
+    } else if (GRP == 0) {
+      // Stage the wave's 32 x D output rows through LDS (its own K/V
+      // buffer) and write them back as whole rows, 16 bytes per lane.
+      char* stg = wave == 0 ? smem_k0[0] : wave == 1 ? smem_v0[0] : wave == 2 ? smem_k1[0] : smem_v1[0];
       // The lane index is re-read here so that the address arithmetic below
       // is not hoisted out of the item loop (it would hold registers there).
       int ln = lane;
@@ -861,6 +997,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     w = __builtin_amdgcn_readfirstlane(sh_item[parity]);  // uniform: keeps item state in SGPRs
     parity ^= 1;
   }
+  };
+  if (KSP == 1 || wave_id < kWaves)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, KSP - 1>{});
   if (dyn) leave_queue(p);
 }
 
@@ -1097,12 +1238,18 @@ int num_cus() {
 using KernelFn = void (*)(KParams);
 
 template <typename T, int D, bool PAGED>
-KernelFn pick16(bool causal, bool rab) {
+KernelFn pick16(bool causal, bool rab, bool ksplit) {
   constexpr int BN = D >= 256 ? 32 : 64;
   constexpr int WPE = D >= 256 ? 1 : 2;
-  if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE> : fwd_kernel<T, D, BN, false, false, true, WPE>;
-  if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE> : fwd_kernel<T, D, BN, true, false, false, WPE>;
-  return rab ? fwd_kernel<T, D, BN, false, true, false, WPE> : fwd_kernel<T, D, BN, false, false, false, WPE>;
+  if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE, 1> : fwd_kernel<T, D, BN, false, false, true, WPE, 1>;
+  if constexpr (BN == 64) {
+    if (ksplit) {
+      if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE, 2> : fwd_kernel<T, D, BN, true, false, false, WPE, 2>;
+      return rab ? fwd_kernel<T, D, BN, false, true, false, WPE, 2> : fwd_kernel<T, D, BN, false, false, false, WPE, 2>;
+    }
+  }
+  if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE, 1> : fwd_kernel<T, D, BN, true, false, false, WPE, 1>;
+  return rab ? fwd_kernel<T, D, BN, false, true, false, WPE, 1> : fwd_kernel<T, D, BN, false, false, false, WPE, 1>;
 }
 
 template <int D, bool PAGED>
@@ -1113,25 +1260,28 @@ KernelFn pick32(bool causal, bool rab) {
   return rab ? fwd_kernel_f32<D, BN, false, true, false> : fwd_kernel_f32<D, BN, false, false, false>;
 }
 
+// ksplit: use the 8-wave key-split kernel (16-bit, head_dim <= 128, jagged).
+// On return, *wgs_per_cu and *threads give the launch shape.
 template <bool PAGED>
-KernelFn pick(DType dt, int D, bool causal, bool rab, int* bn, int* wpe) {
-  *bn = (dt != DType::F32 && D >= 256) ? 32 : 64;
-  *wpe = (dt == DType::F32 || D >= 256) ? 1 : 2;
+KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, int* wgs_per_cu, int* threads) {
+  ksplit = ksplit && !PAGED && dt != DType::F32 && D <= 128;
+  *wgs_per_cu = ksplit ? 1 : ((dt == DType::F32 || D >= 256) ? 1 : 2);
+  *threads = ksplit ? 2 * kThreads : kThreads;
   switch (dt) {
     case DType::BF16:
       switch (D) {
-        case 32: return pick16<__bf16, 32, PAGED>(causal, rab);
-        case 64: return pick16<__bf16, 64, PAGED>(causal, rab);
-        case 128: return pick16<__bf16, 128, PAGED>(causal, rab);
-        case 256: return pick16<__bf16, 256, PAGED>(causal, rab);
+        case 32: return pick16<__bf16, 32, PAGED>(causal, rab, ksplit);
+        case 64: return pick16<__bf16, 64, PAGED>(causal, rab, ksplit);
+        case 128: return pick16<__bf16, 128, PAGED>(causal, rab, ksplit);
+        case 256: return pick16<__bf16, 256, PAGED>(causal, rab, ksplit);
       }
       break;
     case DType::F16:
       switch (D) {
-        case 32: return pick16<_Float16, 32, PAGED>(causal, rab);
-        case 64: return pick16<_Float16, 64, PAGED>(causal, rab);
-        case 128: return pick16<_Float16, 128, PAGED>(causal, rab);
-        case 256: return pick16<_Float16, 256, PAGED>(causal, rab);
+        case 32: return pick16<_Float16, 32, PAGED>(causal, rab, ksplit);
+        case 64: return pick16<_Float16, 64, PAGED>(causal, rab, ksplit);
+        case 128: return pick16<_Float16, 128, PAGED>(causal, rab, ksplit);
+        case 256: return pick16<_Float16, 256, PAGED>(causal, rab, ksplit);
       }
       break;
     case DType::F32:
@@ -1222,7 +1372,7 @@ size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q
 namespace {
 
 KParams make_params(const FwdArgs& a) {
-  KParams p;
+  KParams p = {};
   p.q = a.q;
   p.k = a.k;
   p.v = a.v;
@@ -1272,10 +1422,23 @@ KParams make_params(const FwdArgs& a) {
 
 int tile_n(const FwdArgs& a) { return (a.dtype != DType::F32 && a.head_dim >= 256) ? 32 : 64; }
 
+// Items a run may have: (sequence, q tile, head group) plus split chunks.
+long long item_bound(const FwdArgs& a, const KParams& p) {
+  return ((long long)a.batch * p.n_qt_max + p.split_slots) * p.n_hg;
+}
+
+// Direct mode: when every possible item can have its own CU, the 16-bit
+// jagged kernel takes item w = blockIdx.x from the full grid and no work
+// list is built (the plan phase launches nothing).
+bool use_direct(const FwdArgs& a, const KParams& p) {
+  return !a.paged && a.dtype != DType::F32 && p.split_slots == 0 && item_bound(a, p) <= num_cus();
+}
+
 }  // namespace
 
 hipError_t launch_plan(const FwdArgs& a) {
   const KParams p = make_params(a);
+  if (use_direct(a, p)) return hipSuccess;
   const int bn = tile_n(a);
   if (a.paged)
     hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, a.stream, p, bn, a.causal ? 1 : 0);
@@ -1285,16 +1448,21 @@ hipError_t launch_plan(const FwdArgs& a) {
 }
 
 hipError_t launch_run(const FwdArgs& a) {
-  const KParams p = make_params(a);
-  int bn = 64, wpe = 2;
-  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, &bn, &wpe)
-                        : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, &bn, &wpe);
+  KParams p = make_params(a);
+  const long long upper = item_bound(a, p);
+  if (use_direct(a, p)) p.direct_items = (int32_t)upper;
+  // A work list that cannot give every CU an item runs on the key-split
+  // kernel: one 8-wave workgroup per CU, each item twice as fast.
+  const bool ksplit = upper <= num_cus();
+  int per_cu = 2, threads = kThreads;
+  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, false, &per_cu, &threads)
+                        : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, ksplit, &per_cu, &threads);
   if (!fn) return hipErrorInvalidValue;
-  const long long upper = ((long long)a.batch * p.n_qt_max + p.split_slots) * p.n_hg;
-  const long long cap = (long long)num_cus() * wpe;
+  const long long cap = (long long)num_cus() * per_cu;
   const int grid = (int)(upper < cap ? upper : cap);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, a.stream, p);
+  if (p.direct_items > 0 && grid != p.direct_items) return hipErrorInvalidValue;  // one workgroup per item
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), 0, a.stream, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.split_slots == 0) return err;
   KernelFn red = pick_reduce(a.dtype, a.head_dim, a.paged);
