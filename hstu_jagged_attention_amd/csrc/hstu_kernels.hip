@@ -694,6 +694,8 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       __syncthreads();
       const int j0 = kt * BN;
 
+      // The next tile's DMA goes out first: it has a whole step to land.
+      if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
       // rab for this tile: lane holds row q_loc, keys j0 + 32 jb + 8 a + 4 half + 0..3.
       u32x2_t rv[NJB][4];
       if (RAB) {
@@ -714,7 +716,6 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
             rv[jb][a] = x;
           }
       }
-      if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
       if (!wave_active || !has_tile) return;
 
       const char* kbuf = kv_smem(bufc, 0);
@@ -761,7 +762,8 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       f32x16_t sacc[NJB];
       V8 pf[NJB][2];
       // Epilogue of element r of block jb: rab, mask (masked tiles), SiLU, round.
-      auto epi = [&](auto masked, int jb, int r) {
+      // rab and mask of element r of block jb: y (kept in sacc).
+      auto epi_pre = [&](auto masked, int jb, int r) -> float {
         float y = sacc[jb][r];
         if (RAB) {
           const uint32_t wd = rv[jb][r / 4][(r % 4) / 2];
@@ -784,9 +786,40 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
           const int keep = (int)(vis[jb] << (31 - off)) >> 31;
           y = __builtin_bit_cast(float, __builtin_bit_cast(int, y) & keep);
         }
+        return y;
+      };
+      // Epilogue of element r of block jb: rab, mask (masked tiles), SiLU, round.
+      auto epi = [&](auto masked, int jb, int r) {
+        const float y = epi_pre(masked, jb, r);
         const float e = __builtin_amdgcn_exp2f(y);
         const float pv = y * __builtin_amdgcn_rcpf(1.f + e);
         pf[jb][r / 8][r % 8] = (T)pv;
+      };
+      // The same for the 16 elements of block jb, one operation at a time
+      // across EB elements (each stage its own scheduling region): EB
+      // independent chains, and every result is used EB instructions after
+      // it is made.
+      auto epi_block = [&](auto masked, int jb) {
+        constexpr int EB = RAB ? 8 : 16;  // elements per pass (rab values hold registers too)
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += EB) {
+          float y[EB], e[EB];
+#pragma unroll
+          for (int r = 0; r < EB; ++r) y[r] = epi_pre(masked, jb, r0 + r);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < EB; ++r) e[r] = __builtin_amdgcn_exp2f(y[r]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < EB; ++r) e[r] = 1.f + e[r];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < EB; ++r) e[r] = __builtin_amdgcn_rcpf(e[r]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < EB; ++r) pf[jb][(r0 + r) / 8][(r0 + r) % 8] = (T)(y[r] * e[r]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       };
 
       if constexpr (WPE == 1) {
@@ -845,66 +878,73 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         else
           body(std::true_type{});
       } else {
-        // Two waves per SIMD: keep the register footprint small and let the
-        // other workgroup on the SIMD fill the gaps; only the epilogue
-        // differs between full and masked tiles.
-        // S^T: the key blocks alternate, so consecutive MFMAs are
-        // independent; K fragments are read PF_S MFMAs ahead.
-        constexpr int NS = KS * NJB, PF_S = 4;
+        // Two waves per SIMD: the other wave on the SIMD fills the gaps of
+        // this one. The body is cut into small scheduling regions (by
+        // sched_barrier) whose instruction order is written out here: left
+        // to itself the scheduler chains the SiLU elements one at a time
+        // and reads each MFMA operand just before its MFMA.
+        //
+        // S^T: groups of GS MFMAs (key blocks alternate, so consecutive
+        // MFMAs are independent); the K fragments of group g+1 are read
+        // while group g multiplies.
+        constexpr int NS = KS * NJB;        // S MFMAs per tile
+        constexpr int GS = 2;               // MFMAs per group
+        constexpr int NGS = NS / GS;
+        static_assert(NS % GS == 0, "S groups");
+        auto s_kf = [&](int q) { return k_frag(q % NJB, q / NJB); };  // q-th S MFMA: ks = q / NJB, jb = q % NJB
+        V8 kf[2][GS];
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int e = 0; e < GS; ++e) kf[0][e] = s_kf(e);
 #pragma unroll
-          for (int jb = 0; jb < NJB; ++jb) sacc[jb] = F::mfma(k_frag(jb, ks), qf[ks], sacc[jb]);
-        __builtin_amdgcn_sched_group_barrier(0x100, PF_S, 1);  // DS reads
+        for (int g = 0; g < NGS; ++g) {
+          if (g + 1 < NGS) {
 #pragma unroll
-        for (int q = 0; q < NS - PF_S; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+            for (int e = 0; e < GS; ++e) kf[(g + 1) & 1][e] = s_kf((g + 1) * GS + e);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int e = 0; e < GS; ++e) {
+            const int q = g * GS + e;
+            sacc[q % NJB] = F::mfma(kf[g & 1][e], qf[q / NJB], sacc[q % NJB]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, PF_S, 1);
+        // O^T operands: groups of GP MFMAs in (jb, m, db) order, V^T
+        // fragments one group ahead; group 0 is read during the epilogue.
+        constexpr int NP = NJB * 2 * NDB;
+        constexpr int GP = NDB < 2 ? NDB : 2;
+        constexpr int NGP = NP / GP;
+        static_assert(NDB % GP == 0, "PV groups");
+        auto p_vf = [&](int q) { return v_frag(q / (2 * NDB), (q / NDB) % 2, q % NDB); };
+        V8 vf[2][GP];
+#pragma unroll
+        for (int e = 0; e < GP; ++e) vf[0][e] = p_vf(e);
         auto epi_all = [&](auto masked) {
 #pragma unroll
-          for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) epi(masked, jb, r);
-          if constexpr (!decltype(masked)::value && !RAB) {
-            // Keep eight elements in flight (exp, add, rcp, mul per element,
-            // one packed convert per two): without this the scheduler
-            // chains the elements one after another through one register.
-#pragma unroll
-            for (int g8 = 0; g8 < NJB * 2; ++g8) {
-              __builtin_amdgcn_sched_group_barrier(0x400, 8, 0);  // 8 exp
-              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // 8 add
-              __builtin_amdgcn_sched_group_barrier(0x400, 8, 0);  // 8 rcp
-              __builtin_amdgcn_sched_group_barrier(0x002, 12, 0); // 8 mul, 4 cvt
-            }
-          }
+          for (int jb = 0; jb < NJB; ++jb) epi_block(masked, jb);
         };
-        __builtin_amdgcn_sched_barrier(0);
         if (full)
           epi_all(std::false_type{});
         else
           epi_all(std::true_type{});
-        __builtin_amdgcn_sched_barrier(0);
-        // O^T: V^T fragments (two transposing reads each) PF_V MFMAs ahead.
-        constexpr int NP = NJB * 2 * NDB, PF_V = 4;
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
+        for (int g = 0; g < NGP; ++g) {
+          if (g + 1 < NGP) {
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+            for (int e = 0; e < GP; ++e) vf[(g + 1) & 1][e] = p_vf((g + 1) * GP + e);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] = F::mfma(v_frag(jb, m, db), pf[jb][m], o[db]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF_V, 2);
-#pragma unroll
-        for (int q = 0; q < NP - PF_V; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+          for (int e = 0; e < GP; ++e) {
+            const int q = g * GP + e, jb = q / (2 * NDB), m = (q / NDB) % 2, db = q % NDB;
+            o[db] = F::mfma(vf[g & 1][e], pf[jb][m], o[db]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, PF_V, 2);
       }
     };
 
