@@ -91,7 +91,7 @@ struct KParams {
   int32_t bm;         // query rows per item = 32 * (4 >> hpw_log2)
   int32_t n_qt_max;   // q tiles per sequence, upper bound
   int32_t direct_items; // > 0: no work list; workgroup w runs item w of the
-                        // full (sequence, q tile, head group) grid
+                        // full (q tile descending, sequence, head group) grid
   int32_t ps_log2;    // log2(page_size)
   int32_t g;          // target_group_size
   int32_t rab_vec;    // rab rows allow 4-element vector loads
@@ -552,8 +552,10 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     const int hg = w - item * p.n_hg;
     int b, qt, meta = (1 << 16);  // direct items: one chunk
     if (direct) {
-      b = item / p.n_qt_max;
-      qt = item - b * p.n_qt_max;
+      // Highest q tiles first: under the causal mask they see the most key
+      // tiles, and workgroups start in index order.
+      qt = p.n_qt_max - 1 - item / p.batch;
+      b = item - (p.n_qt_max - 1 - qt) * p.batch;
     } else {
       const int packed = p.items[2 * item];
       meta = p.items[2 * item + 1];

@@ -134,6 +134,36 @@ def test_edge_cases(dev, case):
     assert_parity(got, oracle_jagged(c), dtype, name)
 
 
+# Batches too large for one item per CU run on the work-list path (plan kernel,
+# 4-wave workgroups, queue); the small cases above run on the direct key-split
+# path. The same edge shapes, many sequences at once, cover the former.
+LENGTH_MIX = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 300]
+WORK_LIST = [
+    # (name, Hq, Hk, D, dtype, mask, nc, nt, g, rab)
+    ("mha_bf16_ctx_targets_rab", 2, 2, 128, "bf16", CAUSAL, (0, 12), (0, 40), 1, True),
+    ("gqa_f16_targets_g3", 4, 2, 64, "f16", CAUSAL, None, (1, 30), 3, False),
+    ("bidirectional_bf16_rab", 2, 1, 128, "bf16", NONE, None, None, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", WORK_LIST, ids=[e[0] for e in WORK_LIST])
+def test_work_list_path_edge_mix(dev, case):
+    name, Hq, Hk, D, dtype, mask, nc, nt, g, rab = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    lengths = rng.permutation(np.resize(np.array(LENGTH_MIX), 96))
+    c = wl.jagged_case(zlib.crc32(name.encode()) % (1 << 30), lengths, Hq, Hk, D, dtype, mask_type=mask,
+                       num_context=nc, num_targets=nt, target_group_size=g, rab_std=0.5 if rab else None,
+                       max_seq_len=300)
+    group = Hq // Hk
+    hpw = 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+    bm = 32 * (4 // hpw)
+    items = c.batch * -(-c.max_seq_len // bm) * (Hq // hpw)
+    assert items > torch.cuda.get_device_properties(dev).multi_processor_count, "case must exceed one item per CU"
+    say(name, "batch", c.batch, "items", items)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), dtype, name)
+
+
 def test_every_row_is_written(dev):
     c = wl.jagged_case(5, [45, 0, 200, 1], 4, 2, 128, "bf16", num_targets=(1, 9), target_group_size=1)
     say("every_row_is_written")
