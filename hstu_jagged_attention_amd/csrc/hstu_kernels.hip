@@ -180,17 +180,42 @@ __device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, bool
 // Chunk size: the average work per resident workgroup (at least
 // kMinChunkTiles), doubled until the split items fit the partial-sum slots.
 // ------------------------------------------------------------------------
+// Wave-wide inclusive prefix sum (64 lanes) by DPP lane shifts: within each
+// row of 16 lanes by shifts of 1, 2, 4 and 8, then across rows by the
+// row-broadcasts of lanes 15 and 31. (Cross-lane shuffles through LDS cost
+// several times more; the planner runs dozens of these.)
+__device__ inline int wave_inclusive_sum(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+#endif
+  return x;
+}
+
 // Wave-wide exclusive prefix sum of v (64 lanes); *total gets the wave sum.
 __device__ inline int wave_exclusive_sum(int v, int* total) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  *total = __shfl(x, 63, 64);
+  const int x = wave_inclusive_sum(v);
+  *total = __builtin_amdgcn_readlane(x, 63);
   return x - v;
+}
+
+// Wave-wide maximum of non-negative v.
+__device__ inline int wave_max(int v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+#else
+  return v;
+#endif
 }
 
 // Adds v of every lane to *counter with one atomic per wave; returns the
@@ -200,12 +225,13 @@ __device__ inline int wave_fetch_add(int* counter, int v) {
   const int ex = wave_exclusive_sum(v, &total);
   int base = 0;
   if ((threadIdx.x & 63) == 63 && total != 0) base = atomicAdd(counter, total);
-  base = __shfl(base, 63, 64);
+  base = __builtin_amdgcn_readlane(base, 63);
   return base + ex;
 }
 
 constexpr int kMinChunkTiles = 4;
 constexpr int kCostCache = 4096;  // items whose cost the planner keeps in LDS
+constexpr int kSeqCache = 2048;   // sequences whose lengths the planner keeps in LDS
 
 __device__ inline int item_cost(const Tiles& t) { return t.ta + t.tb1 - t.tb0; }
 
@@ -214,20 +240,54 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
   __shared__ int hist[kMaxBins];  // items per cost, then chunks per cost
   __shared__ int scan[2][kMaxBins];
   __shared__ short cost_cache[kCostCache];
-  __shared__ int count, total_cost, chunk_tiles, slot_alloc, n_split;
+  // Per-sequence lengths (Lq, Lh, H, nc), loaded once: the item loops below
+  // touch every (sequence, q tile) pair, most of which may lie past the end
+  // of their sequence (the q-tile bound comes from max_seq_len).
+  __shared__ int seq_lq[kSeqCache], seq_lh[kSeqCache], seq_h[kSeqCache], seq_nc[kSeqCache];
+  __shared__ int count, total_cost, chunk_tiles, slot_alloc, n_split, qt_bound;
   const int tid = threadIdx.x;
-  const int n_items = p.batch * p.n_qt_max;
   hist[tid] = 0;
   if (tid == 0) {
     count = 0;
     total_cost = 0;
     slot_alloc = 0;
     n_split = 0;
+    qt_bound = p.batch > kSeqCache ? p.n_qt_max : 0;
   }
   __syncthreads();
+  // Sequence lengths, and the largest q-tile count among them (the item
+  // loops below then skip the q tiles no sequence has).
+  for (int b0 = 0; b0 < p.batch && b0 < kSeqCache; b0 += kPlanThreads) {  // uniform trip count
+    const int b = b0 + tid;
+    int nq = 0;
+    if (b < p.batch && b < kSeqCache) {
+      const Seq s = load_seq<PAGED>(p, b, causal != 0);
+      seq_lq[b] = s.Lq;
+      seq_lh[b] = s.Lh;
+      seq_h[b] = s.H;
+      seq_nc[b] = s.nc;
+      nq = (s.Lq + p.bm - 1) / p.bm;
+    }
+    nq = wave_max(nq);
+    if ((tid & 63) == 0) atomicMax(&qt_bound, nq);
+  }
+  __syncthreads();
+  const int n_qt = min(qt_bound, p.n_qt_max);  // q tiles per sequence in the loops below
+  const int n_items = p.batch * n_qt;
+  auto seq_of = [&](int b) -> Seq {
+    if (b >= kSeqCache) return load_seq<PAGED>(p, b, causal != 0);
+    Seq s;
+    s.q_tok0 = s.k_tok0 = s.page0 = 0;  // not used for costing
+    s.Lq = seq_lq[b];
+    s.Lh = seq_lh[b];
+    s.L = s.Lh + s.Lq;
+    s.H = seq_h[b];
+    s.nc = seq_nc[b];
+    return s;
+  };
   auto compute_cost = [&](int idx) -> int {  // -1: no such item
-    const int b = idx / p.n_qt_max, qt = idx - b * p.n_qt_max;
-    const Seq s = load_seq<PAGED>(p, b, causal != 0);
+    const int b = idx / n_qt, qt = idx - b * n_qt;
+    const Seq s = seq_of(b);
     const int q_lo = qt * p.bm;
     if (q_lo >= s.Lq) return -1;
     const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
@@ -252,10 +312,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
   const long long units = (long long)total_cost * p.n_hg;
   const int t0 = (int)min((long long)kMaxBins,
                           max((long long)kMinChunkTiles, (units + p.target_chunks - 1) / p.target_chunks));
-  if (p.split_slots > 0 && hist[tid] > 0) {
+  if (p.split_slots > 0) {  // uniform: every thread takes part in the wave sums
+    const int h = hist[tid];
+#pragma unroll
     for (int ci = 0; ci < kCand; ++ci) {
       const int t = t0 << ci;
-      if (tid > t) atomicAdd(&need[ci], min(hist[tid] * min((tid + t - 1) / t, 255), 1 << 24));
+      wave_fetch_add(&need[ci], (h > 0 && tid > t) ? min(h * min((tid + t - 1) / t, 255), 1 << 24) : 0);
     }
   }
   __syncthreads();
@@ -301,7 +363,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
     const int slot_at = wave_fetch_add(&slot_alloc, split_nk);
     const int split_at = wave_fetch_add(&n_split, split_nk ? 1 : 0);
     if (c < 0) continue;
-    const int b = idx / p.n_qt_max, qt = idx - b * p.n_qt_max;
+    const int b = idx / n_qt, qt = idx - b * n_qt;
     int slot = 0xffff;
     if (nk > 1) {
       slot = slot_at;
