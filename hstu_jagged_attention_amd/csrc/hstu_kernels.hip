@@ -744,7 +744,38 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-    const T* rrow = RAB ? (const T*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + q_loc) * p.max_seq_len : nullptr;
+    // Rows past the sequence read the rab of its last row (always in bounds;
+    // their results are never stored).
+    const T* rrow = RAB ? (const T*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + min(q_loc, max(s.Lq - 1, 0))) *
+                                                p.max_seq_len
+                        : nullptr;
+    // rab of the tile at key j0: lane holds row q_loc, keys j0 + 32 jb + 8 a + 4 half + 0..3.
+    // Loaded one step ahead (issued right after the next tile's DMA), so the
+    // step that uses it never waits for memory in the middle.
+    using RabRegs = u32x2_t[NJB][4];
+    auto load_rab = [&](int j0, RabRegs& rv) {
+      if (j0 + BN <= s.L && p.rab_vec) {  // uniform: whole tile inside the sequence, 8-byte aligned rows
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) rv[jb][a] = *(const u32x2_t*)(rrow + j0 + jb * 32 + 8 * a + 4 * half);
+      } else {
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int jj = j0 + jb * 32 + 8 * a + 4 * half;
+            T t4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t4[e] = (jj + e < s.L) ? rrow[jj + e] : (T)0.f;
+            rv[jb][a] = *(const u32x2_t*)t4;
+          }
+      }
+    };
+    RabRegs rv_next;
+    if constexpr (RAB) {
+      if (n_begin + GRP < n_end) load_rab(tile_at(n_begin + GRP) * BN, rv_next);
+    }
     const int G = lane >> 4, sl = lane & 15;
 
     // One key tile: publish its LDS buffer, request the next tile into the
@@ -758,27 +789,16 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       __syncthreads();
       const int j0 = kt * BN;
 
-      // The next tile's DMA goes out first: it has a whole step to land.
+      // The next tile's DMA goes out first: it has a whole step to land;
+      // then the next tile's rab (this tile's arrived last step).
       if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
-      // rab for this tile: lane holds row q_loc, keys j0 + 32 jb + 8 a + 4 half + 0..3.
-      u32x2_t rv[NJB][4];
-      if (RAB) {
+      RabRegs rv;
+      if constexpr (RAB) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const int jj = j0 + jb * 32 + 8 * a + 4 * half;
-            u32x2_t x = {0u, 0u};
-            if (row_ok && jj + 3 < s.L && p.rab_vec) {
-              x = *(const u32x2_t*)(rrow + jj);
-            } else if (row_ok) {
-              T t4[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) t4[e] = (jj + e < s.L) ? rrow[jj + e] : (T)0.f;
-              x = *(const u32x2_t*)t4;
-            }
-            rv[jb][a] = x;
-          }
+          for (int a = 0; a < 4; ++a) rv[jb][a] = rv_next[jb][a];
+        if (n + KSP < n_end) load_rab(tile_at(n + KSP) * BN, rv_next);
       }
       if (!wave_active || !has_tile) return;
 
@@ -952,7 +972,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         // MFMAs are independent); the K fragments of group g+1 are read
         // while group g multiplies.
         constexpr int NS = KS * NJB;        // S MFMAs per tile
-        constexpr int GS = 2;               // MFMAs per group
+        constexpr int GS = RAB ? 1 : 2;     // MFMAs per group (rab prefetch holds registers)
         constexpr int NGS = NS / GS;
         static_assert(NS % GS == 0, "S groups");
         auto s_kf = [&](int q) { return k_frag(q % NJB, q / NJB); };  // q-th S MFMA: ks = q / NJB, jb = q % NJB
@@ -980,7 +1000,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         // O^T operands: groups of GP MFMAs in (jb, m, db) order, V^T
         // fragments one group ahead; group 0 is read during the epilogue.
         constexpr int NP = NJB * 2 * NDB;
-        constexpr int GP = NDB < 2 ? NDB : 2;
+        constexpr int GP = (RAB || NDB < 2) ? 1 : 2;
         constexpr int NGP = NP / GP;
         static_assert(NDB % GP == 0, "PV groups");
         auto p_vf = [&](int q) { return v_frag(q / (2 * NDB), (q / NDB) % 2, q % NDB); };
