@@ -23,6 +23,7 @@ import torch
 
 MASK_CAUSAL = 0
 MASK_NONE = 2
+MASK_CUSTOM = 3
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -33,11 +34,11 @@ IntSpec = Union[None, int, Sequence[int], tuple]
 class JaggedCase:
     name: str
     dtype: str
-    q: torch.Tensor  # [T, Hq, D]
-    k: torch.Tensor  # [T, Hk, D]
-    v: torch.Tensor  # [T, Hk, D]
-    rab: Optional[torch.Tensor]  # [B, Hq, S, S] or None
-    seq_offsets: np.ndarray  # int64 [B+1]
+    q: torch.Tensor  # [Tq, Hq, D]
+    k: torch.Tensor  # [Tk, Hk, D]
+    v: torch.Tensor  # [Tk, Hk, D]
+    rab: Optional[torch.Tensor]  # [B, Hq or 1, S, S] or None
+    seq_offsets: np.ndarray  # int64 [B+1], queries
     num_context: Optional[np.ndarray]  # int64 [B] or None
     num_targets: Optional[np.ndarray]  # int64 [B] or None
     max_seq_len: int
@@ -45,6 +46,8 @@ class JaggedCase:
     target_group_size: int
     alpha: float
     out_scale: float
+    seq_offsets_k: Optional[np.ndarray] = None  # int64 [B+1], keys (None: same as queries)
+    mask: Optional[torch.Tensor] = None  # [B, Hq or 1, S, S], mask_type 3 only
 
     @property
     def batch(self) -> int:
@@ -52,7 +55,12 @@ class JaggedCase:
 
     @property
     def lengths(self) -> np.ndarray:
+        """Query lengths."""
         return np.diff(self.seq_offsets)
+
+    @property
+    def key_lengths(self) -> np.ndarray:
+        return self.lengths if self.seq_offsets_k is None else np.diff(self.seq_offsets_k)
 
     @property
     def num_heads_q(self) -> int:
@@ -134,12 +142,20 @@ def jagged_case(seed: int, lengths: Sequence[int], num_heads_q: int, num_heads_k
                 dtype: str = "bf16", *, mask_type: int = MASK_CAUSAL, num_context: IntSpec = None,
                 num_targets: IntSpec = None, target_group_size: int = 0, rab_std: Optional[float] = None,
                 rab_padding_nan: bool = True, max_seq_len: Optional[int] = None, alpha: Optional[float] = None,
-                out_scale: Optional[float] = None, name: str = "jagged") -> JaggedCase:
+                out_scale: Optional[float] = None, name: str = "jagged", q_lengths: Optional[Sequence[int]] = None,
+                rab_heads: Optional[int] = None, mask_keep: Optional[float] = None,
+                mask_heads: Optional[int] = None) -> JaggedCase:
     """A jagged case with the given sequence lengths.
 
-    Q, K, V ~ N(0, 1). rab ~ N(0, rab_std^2) when rab_std is given; with
+    Q, K, V ~ N(0, 1). rab ~ N(0, rab_std^2) when rab_std is given, with
+    rab_heads heads (default num_heads_q; 1 = one rab for every head); with
     rab_padding_nan the rab entries outside each sequence (row or column
     >= its length) are NaN, so any read of them poisons the output.
+    q_lengths (optional, each <= the matching entry of lengths) gives the
+    queries of each sequence when they are fewer than its keys: q then holds
+    q_lengths[b] rows per sequence and seq_offsets_k the key offsets.
+    mask_keep (with mask_type 3) draws a user mask [B, mask_heads, S, S] of
+    ones with probability mask_keep, else zeros, NaN outside each sequence.
     alpha defaults to 1/sqrt(head_dim), out_scale to 1/max_seq_len.
     """
     rng = np.random.default_rng(seed)
@@ -151,22 +167,39 @@ def jagged_case(seed: int, lengths: Sequence[int], num_heads_q: int, num_heads_k
     offsets = np.zeros(B + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(lengths)
     T = int(offsets[-1])
-    q = _normal(rng, (T, num_heads_q, head_dim), dtype)
+    offsets_q, offsets_k, Tq = offsets, None, T
+    if q_lengths is not None:
+        ql = np.asarray(q_lengths, dtype=np.int64)
+        assert ql.shape == (B,) and (ql <= lengths).all() and (ql >= 0).all()
+        offsets_q = np.zeros(B + 1, dtype=np.int64)
+        offsets_q[1:] = np.cumsum(ql)
+        offsets_k, Tq = offsets, int(offsets_q[-1])
+    q = _normal(rng, (Tq, num_heads_q, head_dim), dtype)
     k = _normal(rng, (T, num_heads_kv, head_dim), dtype)
     v = _normal(rng, (T, num_heads_kv, head_dim), dtype)
+
+    def padded_nan(x):
+        for b in range(B):
+            x[b, :, lengths[b]:, :] = np.nan
+            x[b, :, :, lengths[b]:] = np.nan
+        return x
+
     rab = None
     if rab_std is not None:
-        x = rng.standard_normal(size=(B, num_heads_q, S, S), dtype=np.float32)
+        x = rng.standard_normal(size=(B, rab_heads or num_heads_q, S, S), dtype=np.float32)
         x *= np.float32(rab_std)
         if rab_padding_nan:
-            for b in range(B):
-                x[b, :, lengths[b]:, :] = np.nan
-                x[b, :, :, lengths[b]:] = np.nan
+            padded_nan(x)
         rab = torch.from_numpy(x).to(TORCH_DTYPES[dtype])
-    return JaggedCase(name=name, dtype=dtype, q=q, k=k, v=v, rab=rab, seq_offsets=offsets, num_context=nc,
+    mask = None
+    if mask_keep is not None:
+        m = (rng.random(size=(B, mask_heads or num_heads_q, S, S), dtype=np.float32) < mask_keep).astype(np.float32)
+        mask = torch.from_numpy(padded_nan(m)).to(TORCH_DTYPES[dtype])
+    return JaggedCase(name=name, dtype=dtype, q=q, k=k, v=v, rab=rab, seq_offsets=offsets_q, num_context=nc,
                       num_targets=nt, max_seq_len=S, mask_type=mask_type, target_group_size=target_group_size,
                       alpha=float(alpha if alpha is not None else 1.0 / math.sqrt(head_dim)),
-                      out_scale=float(out_scale if out_scale is not None else 1.0 / S))
+                      out_scale=float(out_scale if out_scale is not None else 1.0 / S), seq_offsets_k=offsets_k,
+                      mask=mask)
 
 
 def paged_case(seed: int, history_lengths: Sequence[int], new_lengths: Sequence[int], num_heads_q: int,
@@ -274,10 +307,37 @@ def bf16_paged_target(seed: int = 5, batch: int = 64) -> PagedCase:
                       out_scale=1.0 / 4160, name="bf16_paged_target")
 
 
+def bf16_custom_mask(seed: int = 6, batch: int = 16) -> JaggedCase:
+    """The user-mask and rab-broadcast features: batch 16, lengths ~
+    U{256..1024}, 4 heads, d 128, bf16, mask_type 3 with a mask [B, 4, 1024,
+    1024] of ones with probability 1/2, rab [B, 1, 1024, 1024] ~ N(0, 0.1^2)
+    shared by the 4 heads, alpha 1/sqrt(128), out_scale 1/1024."""
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(256, 1024 + 1, size=batch)
+    return jagged_case(seed + 1000, lengths, 4, 4, 128, "bf16", mask_type=MASK_CUSTOM, rab_std=0.1, rab_heads=1,
+                       mask_keep=0.5, max_seq_len=1024, alpha=1.0 / math.sqrt(128), out_scale=1.0 / 1024,
+                       name="bf16_custom_mask")
+
+
+def bf16_delta_qk(seed: int = 7, batch: int = 32) -> JaggedCase:
+    """Different Q and K lengths without paging: batch 32, keys ~
+    U{512..2048} per sequence, of which the last 1..64 are the queries
+    (targets, group size 1), 4 heads, d 128, bf16, causal, no rab, alpha
+    1/sqrt(128), out_scale 1/2048."""
+    rng = np.random.default_rng(seed)
+    lk = rng.integers(512, 2048 + 1, size=batch)
+    lq = rng.integers(1, 64 + 1, size=batch)
+    return jagged_case(seed + 1000, lk, 4, 4, 128, "bf16", mask_type=MASK_CAUSAL, num_targets=lq,
+                       target_group_size=1, max_seq_len=2048, alpha=1.0 / math.sqrt(128), out_scale=1.0 / 2048,
+                       q_lengths=lq, name="bf16_delta_qk")
+
+
 WORKLOADS: Dict[str, Callable[..., object]] = {
     "tiny_fp32_bidirectional": tiny_fp32_bidirectional,
     "bf16_mha_causal": bf16_mha_causal,
     "bf16_rab_target": bf16_rab_target,
     "fp16_gqa_causal": fp16_gqa_causal,
     "bf16_paged_target": bf16_paged_target,
+    "bf16_custom_mask": bf16_custom_mask,
+    "bf16_delta_qk": bf16_delta_qk,
 }

@@ -27,6 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "libhstu_oracle.so")
 
 MASK_CAUSAL = 0
 MASK_NONE = 2
+MASK_CUSTOM = 3
 
 _lib = None
 
@@ -58,7 +59,8 @@ def _load():
     lib.hstu_oracle_vis.restype = ctypes.c_int
     lib.hstu_oracle_mask.argtypes = [I32, I64, I64, I64, I64, P]
     lib.hstu_oracle_mask.restype = None
-    lib.hstu_oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I64, D, D, P, I64]
+    lib.hstu_oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I64, D, D,
+                                    P, I64]
     lib.hstu_oracle_fwd.restype = ctypes.c_int
     lib.hstu_oracle_fwd_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I64, D, D,
                                           P, I64]
@@ -102,16 +104,19 @@ def mask_matrix(mask_type: int, L: int, nc: int = 0, nt: int = 0, g: int = 0) ->
     return out.astype(bool)
 
 
-def hstu_fwd(q, k, v, seq_offsets, *, rab=None, num_context=None, num_targets=None, max_seq_len: int,
-             mask_type: int = MASK_CAUSAL, target_group_size: int = 0, alpha: float = 1.0,
-             out_scale: Optional[float] = None, rows: Optional[Sequence] = None) -> np.ndarray:
+def hstu_fwd(q, k, v, seq_offsets, *, rab=None, mask=None, seq_offsets_k=None, num_context=None,
+             num_targets=None, max_seq_len: int, mask_type: int = MASK_CAUSAL, target_group_size: int = 0,
+             alpha: float = 1.0, out_scale: Optional[float] = None, rows: Optional[Sequence] = None) -> np.ndarray:
     """Jagged forward in float64.
 
-    q [T, Hq, D], k/v [T, Hk, D], rab [B, Hq, max_seq_len, max_seq_len] or None.
-    Returns out [T, Hq, D], or [len(rows), D] when ``rows`` lists (token, head) pairs.
+    q [Tq, Hq, D], k/v [Tk, Hk, D]; seq_offsets for q and seq_offsets_k for
+    k/v (None: the same). rab [B, Hq or 1, max_seq_len, max_seq_len] or None;
+    mask (mask_type 3 only) [B, Hq or 1, max_seq_len, max_seq_len].
+    Returns out [Tq, Hq, D], or [len(rows), D] when ``rows`` lists (token, head) pairs.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     off = _i64(seq_offsets)
+    offk = _i64(seq_offsets_k)
     B = off.shape[0] - 1
     T, Hq, D = q.shape
     Hk = k.shape[1]
@@ -119,12 +124,19 @@ def hstu_fwd(q, k, v, seq_offsets, *, rab=None, num_context=None, num_targets=No
         out_scale = 1.0 / max_seq_len
     rab_a = None if rab is None else _f64(rab)
     if rab_a is not None:
-        assert rab_a.shape == (B, Hq, max_seq_len, max_seq_len), rab_a.shape
+        assert rab_a.shape[0] == B and rab_a.shape[1] in (1, Hq) and rab_a.shape[2:] == (max_seq_len, max_seq_len), \
+            rab_a.shape
+    mask_a = None if mask is None else _f64(mask)
+    if mask_a is not None:
+        assert mask_a.shape[0] == B and mask_a.shape[1] in (1, Hq) and mask_a.shape[2:] == (max_seq_len, max_seq_len), \
+            mask_a.shape
     nc, nt = _i64(num_context), _i64(num_targets)
     rows_a = None if rows is None else _i64(rows).reshape(-1, 2)
     out = np.zeros((T, Hq, D) if rows_a is None else (rows_a.shape[0], D), dtype=np.float64)
-    rc = _load().hstu_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rab_a), _ptr(out), _ptr(off), _ptr(nc), _ptr(nt), B,
-                                 max_seq_len, Hq, Hk, D, mask_type, target_group_size, float(alpha), float(out_scale),
+    rc = _load().hstu_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rab_a), _ptr(mask_a), _ptr(out), _ptr(off),
+                                 _ptr(offk), _ptr(nc), _ptr(nt), B, max_seq_len, Hq, Hk, D,
+                                 1 if rab_a is None else rab_a.shape[1], 1 if mask_a is None else mask_a.shape[1],
+                                 mask_type, target_group_size, float(alpha), float(out_scale),
                                  _ptr(rows_a), 0 if rows_a is None else rows_a.shape[0])
     if rc != 0:
         raise ValueError("oracle: invalid arguments")

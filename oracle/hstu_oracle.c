@@ -31,7 +31,17 @@
  *     max_seq_len;
  *   - GQA maps query head h to kv head floor(h * Hk / Hq) (contiguous groups);
  *   - paged: the new tokens' queries sit right after the cached history,
- *     at absolute positions Lh + t; their keys/values come from k_new/v_new.
+ *     at absolute positions Lh + t; their keys/values come from k_new/v_new;
+ *   - different Q and K lengths (the table's seq_offsets_k and is_delta_qk):
+ *     the Lq queries of a sequence are its last Lq positions, i.e. query t
+ *     sits at absolute position Lk - Lq + t among the Lk keys (Lq <= Lk);
+ *   - rab and the user mask may have one head ([B, 1, S, S], the feature
+ *     table's rab broadcast), which then serves every query head; they are
+ *     indexed by absolute positions (i, j);
+ *   - mask_type 3 (user mask, the table's mask input [B, N, S, S]): every key
+ *     of the sequence is a candidate and the mask value m = mask[b,h,i,j]
+ *     multiplies P; m == 0 removes the key entirely (it contributes exactly
+ *     zero, whatever the score), as the built-in masks do.
  *
  * Every function is a direct loop over the definition; no blocking, no
  * reordering beyond summation order in j and e.
@@ -43,6 +53,7 @@
 
 #define ORACLE_MASK_CAUSAL 0
 #define ORACLE_MASK_NONE 2
+#define ORACLE_MASK_CUSTOM 3
 
 /* SiLU, textbook form x * sigmoid(x). */
 double hstu_oracle_silu(double x) { return x / (1.0 + exp(-x)); }
@@ -51,7 +62,7 @@ double hstu_oracle_silu(double x) { return x / (1.0 + exp(-x)); }
  * length L, under the reading stated in the header comment. */
 int hstu_oracle_vis(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int64_t g, int64_t i, int64_t j) {
   if (i < 0 || j < 0 || i >= L || j >= L) return 0;
-  if (mask_type == ORACLE_MASK_NONE) return 1;
+  if (mask_type != ORACLE_MASK_CAUSAL) return 1; /* none, or the user mask decides */
   if (nt < 0) nt = 0;
   if (nt > L) nt = L;
   int64_t H = L - nt;
@@ -71,15 +82,19 @@ void hstu_oracle_mask(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int6
 /* One output row: query row qrow (pointer to D values), keys/values given as
  * per-position row pointers through a callback-free array of row pointers. */
 static void one_row(const double* qrow, const double* const* krows, const double* const* vrows,
-                    const double* rabrow /* nullable, indexed by local j */, int64_t L, int64_t D, int32_t mask_type,
-                    int64_t nc, int64_t nt, int64_t g, int64_t i, double alpha, double out_scale, double* out) {
+                    const double* rabrow /* nullable, indexed by local j */,
+                    const double* maskrow /* nullable (mask_type 3), indexed by local j */, int64_t L, int64_t D,
+                    int32_t mask_type, int64_t nc, int64_t nt, int64_t g, int64_t i, double alpha, double out_scale,
+                    double* out) {
   for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
   for (int64_t j = 0; j < L; ++j) {
     if (!hstu_oracle_vis(mask_type, L, nc, nt, g, i, j)) continue;
+    if (maskrow && maskrow[j] == 0.0) continue;
     double s = 0.0;
     for (int64_t e = 0; e < D; ++e) s += qrow[e] * krows[j][e];
     if (rabrow) s += rabrow[j];
     double p = hstu_oracle_silu(alpha * s);
+    if (maskrow) p *= maskrow[j];
     for (int64_t d = 0; d < D; ++d) out[d] += p * vrows[j][d];
   }
   for (int64_t d = 0; d < D; ++d) out[d] *= out_scale;
@@ -87,19 +102,26 @@ static void one_row(const double* qrow, const double* const* krows, const double
 
 /*
  * Jagged forward.
- *   q   [T, Hq, D], k, v [T, Hk, D]  (float64, contiguous)
- *   rab [B, Hq, max_seq_len, max_seq_len] or NULL
- *   out [T, Hq, D]
- *   seq_offsets [B+1]; num_context, num_targets [B] or NULL.
+ *   q   [Tq, Hq, D], k, v [Tk, Hk, D]  (float64, contiguous)
+ *   rab [B, rab_heads, max_seq_len, max_seq_len] or NULL (rab_heads 1 or Hq)
+ *   mask [B, mask_heads, max_seq_len, max_seq_len], mask_type 3 only
+ *   out [Tq, Hq, D]
+ *   seq_offsets [B+1] (queries); seq_offsets_k [B+1] (keys) or NULL (same);
+ *   num_context, num_targets [B] or NULL.
  * If rows != NULL, only the n_rows (token, head) pairs listed in rows[2*r],
  * rows[2*r+1] are computed, into out[r*D ...] (sampled mode); otherwise all.
  * Returns 0 on success, -1 on invalid arguments.
  */
-int hstu_oracle_fwd(const double* q, const double* k, const double* v, const double* rab, double* out,
-                    const int64_t* seq_offsets, const int64_t* num_context, const int64_t* num_targets, int64_t B,
-                    int64_t max_seq_len, int64_t Hq, int64_t Hk, int64_t D, int32_t mask_type, int64_t g, double alpha,
-                    double out_scale, const int64_t* rows, int64_t n_rows) {
+int hstu_oracle_fwd(const double* q, const double* k, const double* v, const double* rab, const double* mask,
+                    double* out, const int64_t* seq_offsets, const int64_t* seq_offsets_k,
+                    const int64_t* num_context, const int64_t* num_targets, int64_t B, int64_t max_seq_len, int64_t Hq,
+                    int64_t Hk, int64_t D, int64_t rab_heads, int64_t mask_heads, int32_t mask_type, int64_t g,
+                    double alpha, double out_scale, const int64_t* rows, int64_t n_rows) {
   if (B < 0 || Hq <= 0 || Hk <= 0 || D <= 0 || Hq % Hk != 0) return -1;
+  if ((mask_type == ORACLE_MASK_CUSTOM) != (mask != NULL)) return -1;
+  if (rab && rab_heads != 1 && rab_heads != Hq) return -1;
+  if (mask && mask_heads != 1 && mask_heads != Hq) return -1;
+  const int64_t* koff = seq_offsets_k ? seq_offsets_k : seq_offsets;
   const int64_t T = seq_offsets[B];
   int64_t n_items = rows ? n_rows : T * Hq;
   int err = 0;
@@ -118,17 +140,25 @@ int hstu_oracle_fwd(const double* q, const double* k, const double* v, const dou
       err = 1;
       continue;
     }
-    const int64_t s0 = seq_offsets[b], L = seq_offsets[b + 1] - s0, i = t - s0;
+    const int64_t q0 = seq_offsets[b], Lq = seq_offsets[b + 1] - q0;
+    const int64_t k0 = koff[b], L = koff[b + 1] - k0;
+    if (Lq > L) {
+      err = 1;
+      continue;
+    }
+    const int64_t i = L - Lq + (t - q0); /* absolute position among the keys */
     const int64_t hk = h * Hk / Hq;
     const int64_t nc = num_context ? num_context[b] : 0, nt = num_targets ? num_targets[b] : 0;
     const double** kr = (const double**)malloc(sizeof(double*) * (size_t)(L > 0 ? L : 1));
     const double** vr = (const double**)malloc(sizeof(double*) * (size_t)(L > 0 ? L : 1));
     for (int64_t j = 0; j < L; ++j) {
-      kr[j] = k + ((s0 + j) * Hk + hk) * D;
-      vr[j] = v + ((s0 + j) * Hk + hk) * D;
+      kr[j] = k + ((k0 + j) * Hk + hk) * D;
+      vr[j] = v + ((k0 + j) * Hk + hk) * D;
     }
-    const double* rabrow = rab ? rab + ((b * Hq + h) * max_seq_len + i) * max_seq_len : NULL;
-    one_row(q + (t * Hq + h) * D, kr, vr, rabrow, L, D, mask_type, nc, nt, g, i, alpha, out_scale, o);
+    const int64_t hr = rab_heads == 1 ? 0 : h, hm = mask_heads == 1 ? 0 : h;
+    const double* rabrow = rab ? rab + ((b * rab_heads + hr) * max_seq_len + i) * max_seq_len : NULL;
+    const double* maskrow = mask ? mask + ((b * mask_heads + hm) * max_seq_len + i) * max_seq_len : NULL;
+    one_row(q + (t * Hq + h) * D, kr, vr, rabrow, maskrow, L, D, mask_type, nc, nt, g, i, alpha, out_scale, o);
     free(kr);
     free(vr);
   }
@@ -187,7 +217,7 @@ int hstu_oracle_fwd_paged(const double* q, const double* k_new, const double* v_
       kr[Lh + j] = k_new + ((q0 + j) * Hk + hk) * D;
       vr[Lh + j] = v_new + ((q0 + j) * Hk + hk) * D;
     }
-    one_row(q + (t * Hq + h) * D, kr, vr, NULL, L, D, mask_type, nc, nt, g, i, alpha, out_scale, o);
+    one_row(q + (t * Hq + h) * D, kr, vr, NULL, NULL, L, D, mask_type, nc, nt, g, i, alpha, out_scale, o);
     free(kr);
     free(vr);
   }

@@ -7,6 +7,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 from scipy.special import expit
 
 import oracle
@@ -136,7 +137,8 @@ def small_case(seed, lengths, Hq=2, Hk=2, D=8, mask=CAUSAL, nc=None, nt=None, g=
 
 
 def run_oracle(c, q=None, k=None, v=None, **over):
-    kw = dict(rab=None if c.rab is None else f64(c.rab), num_context=c.num_context, num_targets=c.num_targets,
+    kw = dict(rab=None if c.rab is None else f64(c.rab), mask=None if c.mask is None else f64(c.mask),
+              seq_offsets_k=c.seq_offsets_k, num_context=c.num_context, num_targets=c.num_targets,
               max_seq_len=c.max_seq_len, mask_type=c.mask_type, target_group_size=c.target_group_size,
               alpha=c.alpha, out_scale=c.out_scale)
     kw.update(over)
@@ -468,3 +470,157 @@ def test_metrics_counts_match_oracle_mask():
         for mt in (CAUSAL, NONE):
             M = oracle.mask_matrix(mt, L, nc, nt, g)
             np.testing.assert_array_equal(metrics.visible_per_row(L, nc, nt, g, mt), M.sum(1))
+
+
+# ------------------------------------------ user mask, rab broadcast, delta-QK
+CUSTOM = oracle.MASK_CUSTOM
+
+
+def dense_general(c):
+    """Per sequence and head, with BLAS matmul and scipy's logistic function:
+    the queries are the last Lq of the Lk positions (rows Lk-Lq.. of the
+    full score matrix); rab / mask heads broadcast when they have one head;
+    the user mask M multiplies P where it is non-zero and removes the key
+    where it is zero; the built-in mask comes from the rule-based sets."""
+    q, k, v = f64(c.q), f64(c.k), f64(c.v)
+    rab = None if c.rab is None else f64(c.rab)
+    um = None if c.mask is None else f64(c.mask)
+    koff = c.seq_offsets if c.seq_offsets_k is None else c.seq_offsets_k
+    Hq, Hk = q.shape[1], k.shape[1]
+    out = np.zeros_like(q)
+    for b in range(c.batch):
+        q0, q1, k0, k1 = c.seq_offsets[b], c.seq_offsets[b + 1], koff[b], koff[b + 1]
+        Lq, L = q1 - q0, k1 - k0
+        rows = np.arange(L - Lq, L)
+        nc = 0 if c.num_context is None else c.num_context[b]
+        nt = 0 if c.num_targets is None else c.num_targets[b]
+        M = mask_from_rules(L, nc, nt, c.target_group_size, NONE if c.mask_type == CUSTOM else c.mask_type)[rows]
+        for h in range(Hq):
+            hk = h * Hk // Hq
+            S = q[q0:q1, h, :] @ k[k0:k1, hk, :].T
+            keep = M.copy()
+            scale = np.ones_like(S)
+            if um is not None:
+                mm = um[b, 0 if um.shape[1] == 1 else h][np.ix_(rows, np.arange(L))]
+                keep &= mm != 0
+                scale = np.where(keep, mm, 0.0)
+            if rab is not None:
+                rr = rab[b, 0 if rab.shape[1] == 1 else h][np.ix_(rows, np.arange(L))]
+                S = S + np.where(keep, rr, 0.0)
+            X = c.alpha * S
+            P = np.where(keep, X * expit(X) * scale, 0.0)
+            out[q0:q1, h, :] = c.out_scale * (P @ v[k0:k1, hk, :])
+    return out
+
+
+def custom_case(seed, lengths, keep=0.5, Hq=2, Hk=2, rab=True, rab_heads=None, mask_heads=None, S=None):
+    return wl.jagged_case(seed, lengths, Hq, Hk, 8, "f32", mask_type=CUSTOM, rab_std=0.5 if rab else None,
+                          rab_heads=rab_heads, mask_keep=keep, mask_heads=mask_heads, max_seq_len=S, alpha=0.7,
+                          out_scale=0.3)
+
+
+@pytest.mark.parametrize("kind", ["mask", "mask_gqa_bcast", "mask_values", "delta_causal", "delta_ctx_tgt_rab",
+                                  "delta_none_gqa", "delta_mask"])
+def test_general_oracle_matches_dense_library(kind):
+    """The user mask, rab broadcast and delta-QK paths of the oracle against
+    the dense BLAS formulation (the inputs/outputs table: mask
+    [B, N, S, S] with mask_type 3, rab broadcast [b, 1, s, s], seq_offsets_k
+    with is_delta_qk)."""
+    if kind == "mask":
+        c = custom_case(11, [13, 1, 20, 0], S=24)
+    elif kind == "mask_gqa_bcast":
+        c = custom_case(12, [9, 16], Hq=4, Hk=2, rab_heads=1, mask_heads=1)
+    elif kind == "mask_values":
+        c = custom_case(13, [7, 12], keep=0.6)
+        rng = np.random.default_rng(0)  # scale the kept entries by values other than 1, some negative
+        c.mask = c.mask * torch.from_numpy(rng.choice([0.5, 2.0, -1.5], size=tuple(c.mask.shape)).astype(np.float32))
+    elif kind == "delta_causal":
+        c = wl.jagged_case(14, [17, 30, 5], 2, 2, 8, "f32", q_lengths=[4, 30, 1], alpha=0.7, out_scale=0.3)
+    elif kind == "delta_ctx_tgt_rab":
+        c = wl.jagged_case(15, [21, 26], 2, 2, 8, "f32", q_lengths=[9, 3], num_context=(0, 6), num_targets=(1, 8),
+                           target_group_size=2, rab_std=0.5, max_seq_len=28, alpha=0.7, out_scale=0.3)
+    elif kind == "delta_none_gqa":
+        c = wl.jagged_case(16, [12, 19], 6, 2, 8, "f32", q_lengths=[12, 2], mask_type=NONE, alpha=0.7, out_scale=0.3)
+    else:
+        c = wl.jagged_case(17, [15, 22], 2, 2, 8, "f32", q_lengths=[6, 5], mask_type=CUSTOM, mask_keep=0.5,
+                           rab_std=0.5, rab_heads=1, alpha=0.7, out_scale=0.3)
+    np.testing.assert_allclose(run_oracle(c), dense_general(c), rtol=1e-12, atol=1e-13)
+
+
+def test_user_mask_of_ones_is_no_mask():
+    c = custom_case(21, [11, 17], keep=1.0, rab=False)
+    got = run_oracle(c)
+    ref = run_oracle(c, mask=None, mask_type=NONE)
+    assert np.array_equal(got, ref)
+
+
+def test_user_mask_of_rule_sets_is_the_builtin_mask():
+    """A user mask holding the 0/1 matrix built from the English mask rules
+    reproduces the built-in causal mask with context and target groups."""
+    lengths, nc, nt, g = [19, 24, 7], [3, 0, 2], [5, 9, 0], 3
+    c = wl.jagged_case(22, lengths, 2, 2, 8, "f32", mask_type=CAUSAL, num_context=nc, num_targets=nt,
+                       target_group_size=g, alpha=0.7, out_scale=0.3)
+    S = max(lengths)
+    m = np.zeros((len(lengths), 1, S, S))
+    for b, L in enumerate(lengths):
+        m[b, 0, :L, :L] = mask_from_rules(L, nc[b], nt[b], g, CAUSAL)
+    builtin = run_oracle(c)
+    user = run_oracle(c, mask=m, mask_type=CUSTOM, num_context=None, num_targets=None, max_seq_len=S)
+    assert np.array_equal(builtin, user)
+
+
+def test_user_mask_scales_linearly():
+    c = custom_case(23, [10, 14], keep=1.0)
+    ones = run_oracle(c)
+    twos = run_oracle(c, mask=2.0 * f64(c.mask))
+    np.testing.assert_allclose(twos, 2.0 * ones, rtol=1e-14, atol=0)
+
+
+def test_user_mask_zero_removes_nan_scores():
+    """Zero mask entries contribute exactly zero even where rab is NaN."""
+    c = custom_case(24, [12, 9], keep=0.5)
+    clean = run_oracle(c)
+    rab = f64(c.rab).copy()
+    m = f64(c.mask)
+    rab[np.nan_to_num(m, nan=1.0) == 0] = np.nan
+    got = run_oracle(c, rab=rab)
+    assert np.isfinite(got).all()
+    assert np.array_equal(got, clean)
+
+
+def test_zero_user_mask_gives_zero():
+    c = custom_case(25, [8, 13], keep=0.0)
+    assert not run_oracle(c).any()
+
+
+def test_rab_broadcast_equals_repeated_rab():
+    c = custom_case(26, [9, 14], Hq=3, Hk=1, rab_heads=1)
+    rep = np.repeat(f64(c.rab), 3, axis=1)
+    assert np.array_equal(run_oracle(c), run_oracle(c, rab=rep))
+
+
+def test_delta_qk_equals_last_rows_of_full_sequence():
+    """Queries right-aligned on the keys: the delta call equals the full
+    call's rows for the last Lq positions (same keys, same mask inputs)."""
+    lk, lq = [20, 33, 7], [5, 33, 1]
+    full = wl.jagged_case(27, lk, 2, 2, 8, "f32", num_context=(0, 4), num_targets=(1, 6), target_group_size=1,
+                          rab_std=0.5, max_seq_len=34, alpha=0.7, out_scale=0.3)
+    qf = f64(full.q)
+    rows = np.concatenate([np.arange(full.seq_offsets[b + 1] - lq[b], full.seq_offsets[b + 1]) for b in range(3)])
+    offq = np.concatenate([[0], np.cumsum(lq)])
+    ref = run_oracle(full)[rows]
+    got = oracle.hstu_fwd(qf[rows], f64(full.k), f64(full.v), offq, seq_offsets_k=full.seq_offsets,
+                          rab=f64(full.rab), num_context=full.num_context, num_targets=full.num_targets,
+                          max_seq_len=34, mask_type=CAUSAL, target_group_size=1, alpha=0.7, out_scale=0.3)
+    assert np.array_equal(got, ref)
+
+
+def test_general_oracle_rejects_bad_arguments():
+    c = custom_case(28, [5, 6])
+    with pytest.raises(ValueError):  # mask_type 3 needs a mask
+        run_oracle(c, mask=None)
+    with pytest.raises(ValueError):  # a mask needs mask_type 3
+        run_oracle(c, mask_type=NONE)
+    d = wl.jagged_case(29, [4, 6], 2, 2, 8, "f32", alpha=0.7, out_scale=0.3)
+    with pytest.raises(ValueError):  # more queries than keys
+        oracle.hstu_fwd(f64(d.q), f64(d.k)[:8], f64(d.v)[:8], d.seq_offsets, seq_offsets_k=[0, 3, 8], max_seq_len=6)
