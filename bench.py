@@ -108,18 +108,41 @@ def build_step(name, dev):
                     total_new_tokens=Tq, total_history_tokens=int(c.history_lengths.sum()))
     else:
         prep = hj.prepare_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets),
-                              rab=None if c.rab is None else c.rab.to(dev), num_context=c.num_context,
-                              num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
-                              target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
-        pairs = metrics.pairs_jagged(c.seq_offsets, c.num_context, c.num_targets, c.target_group_size, c.mask_type)
-        T = int(c.seq_offsets[-1])
-        alg_bytes = metrics.algorithmic_bytes_jagged(T, c.num_heads_q, c.num_heads_kv, c.head_dim, ELEM[c.dtype],
-                                                     pairs if c.rab is not None else 0)
+                              rab=None if c.rab is None else c.rab.to(dev),
+                              mask=None if c.mask is None else c.mask.to(dev),
+                              seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
+                              num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                              mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                              out_scale=c.out_scale)
+        T, Tk = int(c.seq_offsets[-1]), int(c.key_lengths.sum())
+        E = ELEM[c.dtype]
+        if c.mask is not None:
+            m = c.mask.float().numpy()
+            total, rab_entries = metrics.user_mask_counts(m, c.lengths, c.num_heads_q,
+                                                          0 if c.rab is None else int(c.rab.shape[1]))
+            pairs = total / c.num_heads_q
+            in_seq = float(sum(int(L) ** 2 for L in c.lengths)) * m.shape[1]
+            alg_bytes = metrics.algorithmic_bytes_jagged(T, c.num_heads_q, c.num_heads_kv, c.head_dim, E,
+                                                         extra_bytes=(in_seq + rab_entries) * E)
+        else:
+            if c.seq_offsets_k is None:
+                pairs = metrics.pairs_jagged(c.seq_offsets, c.num_context, c.num_targets, c.target_group_size,
+                                             c.mask_type)
+            else:
+                pairs = metrics.pairs_delta(c.key_lengths, c.lengths, c.num_context, c.num_targets,
+                                            c.target_group_size, c.mask_type)
+            alg_bytes = metrics.algorithmic_bytes_jagged(T, c.num_heads_q, c.num_heads_kv, c.head_dim, E,
+                                                         pairs if c.rab is not None else 0, Tk=Tk)
         desc = dict(batch=c.batch, total_tokens=T, max_seq_len=c.max_seq_len, lengths_min=int(c.lengths.min()),
                     lengths_max=int(c.lengths.max()))
+        if c.seq_offsets_k is not None:
+            desc.update(total_key_tokens=Tk, key_lengths_min=int(c.key_lengths.min()),
+                        key_lengths_max=int(c.key_lengths.max()))
+        if c.mask is not None:
+            desc.update(user_mask_heads=int(c.mask.shape[1]), rab_heads=0 if c.rab is None else int(c.rab.shape[1]))
     flops = metrics.effective_flops(pairs, c.num_heads_q, c.head_dim)
     desc.update(num_heads_q=c.num_heads_q, num_heads_kv=c.num_heads_kv, head_dim=c.head_dim,
-                mask="causal" if c.mask_type == 0 else "bidirectional", rab=bool(getattr(c, "rab", None) is not None),
+                mask={0: "causal", 2: "bidirectional", 3: "user mask"}[c.mask_type], rab=bool(getattr(c, "rab", None) is not None),
                 visible_pairs_per_head=pairs)
     return c, prep, flops, alg_bytes, desc
 
@@ -141,9 +164,12 @@ def cpu_baseline(c, name, flops_full):
                                             target_group_size=c.target_group_size, alpha=c.alpha,
                                             out_scale=c.out_scale)
         sample, fl = "whole workload", flops_full
-    elif name in ("bf16_mha_causal", "tiny_fp32_bidirectional"):
+    elif name in ("bf16_mha_causal", "tiny_fp32_bidirectional", "bf16_custom_mask", "bf16_delta_qk"):
         q, k, v = f64(c.q), f64(c.k), f64(c.v)
-        run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, num_context=c.num_context, num_targets=c.num_targets,
+        rab = None if c.rab is None else f64(c.rab)
+        mask = None if c.mask is None else f64(c.mask)
+        run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, mask=mask, seq_offsets_k=c.seq_offsets_k,
+                                      num_context=c.num_context, num_targets=c.num_targets,
                                       max_seq_len=c.max_seq_len, mask_type=c.mask_type,
                                       target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
         sample, fl = "whole workload", flops_full
@@ -248,7 +274,7 @@ def main():
         copy_calibration(dev)
         return
     names = ["tiny_fp32_bidirectional", "bf16_mha_causal", "bf16_rab_target", "fp16_gqa_causal",
-             "bf16_paged_target"] if args.all else [args.workload]
+             "bf16_paged_target", "bf16_custom_mask", "bf16_delta_qk"] if args.all else [args.workload]
     for name in names:
         print(f"[bench] {name}: building inputs", file=sys.stderr, flush=True)
         res = measure(name, args, dev)

@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libhstu.so")
 
 MASK_CAUSAL = 0
 MASK_NONE = 2
+MASK_CUSTOM = 3
 
 HSTU_OK = 0
 HSTU_ERR_INVALID_ARG = 1
@@ -68,7 +69,7 @@ def load_library(path: Optional[str] = None):
     lib.hstu_fwd_workspace_size.restype = SZ
     lib.hstu_fwd_paged_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, E]
     lib.hstu_fwd_paged_workspace_size.restype = SZ
-    jag = [P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, E, I32, F, F, E, P, SZ, P]
+    jag = [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, E, I32, F, F, E, P, SZ, P]
     pag = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, F, F, E, P, SZ, P]
     for name in ("hstu_fwd", "hstu_fwd_run"):
         getattr(lib, name).argtypes = jag
@@ -76,7 +77,7 @@ def load_library(path: Optional[str] = None):
     for name in ("hstu_fwd_paged", "hstu_fwd_paged_run"):
         getattr(lib, name).argtypes = pag
         getattr(lib, name).restype = E
-    lib.hstu_fwd_plan.argtypes = [P, P, P, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
+    lib.hstu_fwd_plan.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
     lib.hstu_fwd_plan.restype = E
     lib.hstu_fwd_paged_plan.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
     lib.hstu_fwd_paged_plan.restype = E
@@ -171,13 +172,18 @@ class Prepared:
 
 
 def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, *, rab: Optional[torch.Tensor] = None,
-                num_context=None, num_targets=None, max_seq_len: Optional[int] = None, mask_type: int = MASK_CAUSAL,
-                target_group_size: int = 0, alpha: float = 1.0, out_scale: Optional[float] = None,
-                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> Prepared:
-    """Marshal a jagged forward: q [T, Hq, D], k/v [T, Hk, D] on the GPU.
+                mask: Optional[torch.Tensor] = None, seq_offsets_k=None, num_context=None, num_targets=None,
+                max_seq_len: Optional[int] = None, mask_type: Optional[int] = None, target_group_size: int = 0,
+                alpha: float = 1.0, out_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Prepared:
+    """Marshal a jagged forward: q [Tq, Hq, D], k/v [Tk, Hk, D] on the GPU.
 
-    max_seq_len defaults to the longest sequence (read back from the device:
-    pass it explicitly to avoid that synchronisation)."""
+    seq_offsets addresses q; seq_offsets_k (optional) addresses k/v when the
+    query and key lengths differ (queries are the last positions of each
+    sequence). rab and mask are [B, Hq or 1, max_seq_len, max_seq_len].
+    mask_type defaults to MASK_CUSTOM when a mask is given, else MASK_CAUSAL.
+    max_seq_len defaults to the longest key sequence (read back from the
+    device: pass it explicitly to avoid that synchronisation)."""
     lib = load_library()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [tokens, heads, head_dim]")
@@ -188,15 +194,27 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
     _dev_tensor(k, "k", dtype, device)
     _dev_tensor(v, "v", dtype, device)
     off = _int32(seq_offsets, "seq_offsets", device)
+    offk = _int32(seq_offsets_k, "seq_offsets_k", device)
     B = int(off.shape[0]) - 1
+    if offk is not None and int(offk.shape[0]) != B + 1:
+        raise ValueError("seq_offsets_k must have batch + 1 entries")
+    if mask_type is None:
+        mask_type = MASK_CUSTOM if mask is not None else MASK_CAUSAL
     if max_seq_len is None:
-        max_seq_len = int((off[1:] - off[:-1]).max().item()) if B > 0 else 1
+        ko = off if offk is None else offk
+        max_seq_len = int((ko[1:] - ko[:-1]).max().item()) if B > 0 else 1
     if out_scale is None:
         out_scale = 1.0 / max_seq_len
-    if rab is not None:
-        _dev_tensor(rab, "rab", dtype, device)
-        if tuple(rab.shape) != (B, q.shape[1], max_seq_len, max_seq_len):
-            raise ValueError(f"rab must be [{B}, {q.shape[1]}, {max_seq_len}, {max_seq_len}], got {tuple(rab.shape)}")
+    heads = {}
+    for name, t in (("rab", rab), ("mask", mask)):
+        heads[name] = 1
+        if t is not None:
+            _dev_tensor(t, name, dtype, device)
+            if t.dim() != 4 or t.shape[0] != B or t.shape[1] not in (1, q.shape[1]) or \
+                    tuple(t.shape[2:]) != (max_seq_len, max_seq_len):
+                raise ValueError(f"{name} must be [{B}, {q.shape[1]} or 1, {max_seq_len}, {max_seq_len}], "
+                                 f"got {tuple(t.shape)}")
+            heads[name] = int(t.shape[1])
     nc = _int32(num_context, "num_context", device)
     nt = _int32(num_targets, "num_targets", device)
     if out is None:
@@ -210,12 +228,12 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     wsb = workspace.numel() * workspace.element_size()
     stream = _stream(device)
-    fwd_args = (_ptr(q), _ptr(k), _ptr(v), _ptr(rab), _ptr(out), _ptr(off), _ptr(nc), _ptr(nt), B, max_seq_len, Hq,
-                Hk, D, int(mask_type), int(target_group_size), float(alpha), float(out_scale), code, _ptr(workspace),
-                wsb, stream)
-    plan_args = (_ptr(off), _ptr(nc), _ptr(nt), B, max_seq_len, Hq, Hk, D, int(mask_type), int(target_group_size),
-                 code, _ptr(workspace), wsb, stream)
-    return Prepared("hstu_fwd", lib, fwd_args, plan_args, out, workspace, (q, k, v, rab, off, nc, nt))
+    fwd_args = (_ptr(q), _ptr(k), _ptr(v), _ptr(rab), _ptr(mask), _ptr(out), _ptr(off), _ptr(offk), _ptr(nc),
+                _ptr(nt), B, max_seq_len, Hq, Hk, D, heads["rab"], heads["mask"], int(mask_type),
+                int(target_group_size), float(alpha), float(out_scale), code, _ptr(workspace), wsb, stream)
+    plan_args = (_ptr(off), _ptr(offk), _ptr(nc), _ptr(nt), B, max_seq_len, Hq, Hk, D, int(mask_type),
+                 int(target_group_size), code, _ptr(workspace), wsb, stream)
+    return Prepared("hstu_fwd", lib, fwd_args, plan_args, out, workspace, (q, k, v, rab, mask, off, offk, nc, nt))
 
 
 def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, **kw) -> torch.Tensor:

@@ -36,14 +36,14 @@ hstu_status_t check_common(int32_t batch, int32_t max_seq_len, int32_t hq, int32
                            const int32_t* num_targets) {
   if (batch < 0 || hq < 0 || d < 0 || hk < 0 || max_seq_len < 0 || group_size < 0) return HSTU_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return HSTU_ERR_UNSUPPORTED;
-  if (mask != HSTU_MASK_CAUSAL && mask != HSTU_MASK_NONE) {
-    return (mask == 1 || mask == 3) ? HSTU_ERR_UNSUPPORTED : HSTU_ERR_INVALID_ARG;
+  if (mask != HSTU_MASK_CAUSAL && mask != HSTU_MASK_NONE && mask != HSTU_MASK_CUSTOM) {
+    return mask == 1 ? HSTU_ERR_UNSUPPORTED : HSTU_ERR_INVALID_ARG;
   }
   if (batch == 0 || hq == 0 || d == 0) return HSTU_OK;  // empty input: nothing runs
   if (hk <= 0 || hq % hk != 0) return HSTU_ERR_INVALID_ARG;
   if (max_seq_len < 1 || max_seq_len > kMaxSeqLen) return HSTU_ERR_INVALID_ARG;
   if (!head_dim_ok(d, dtype)) return HSTU_ERR_UNSUPPORTED;
-  if (mask == HSTU_MASK_NONE && (num_context || num_targets)) return HSTU_ERR_INVALID_ARG;
+  if (mask != HSTU_MASK_CAUSAL && (num_context || num_targets)) return HSTU_ERR_INVALID_ARG;
   if ((num_context && !aligned4(num_context)) || (num_targets && !aligned4(num_targets))) return HSTU_ERR_INVALID_ARG;
   return HSTU_OK;
 }
@@ -83,20 +83,28 @@ hstu_status_t enqueue(const hstu::FwdArgs& a, int phase) {
 
 // Jagged entry points share this body. Pointers a run does not need (q, k,
 // v, out) may be NULL in the plan-only phase.
-hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, const void* rab, void* out,
-                     const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets, int32_t batch,
-                     int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                     hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
-                     hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, const void* rab, const void* mask,
+                     void* out, const int32_t* seq_offsets, const int32_t* seq_offsets_k,
+                     const int32_t* num_context, const int32_t* num_targets, int32_t batch, int32_t max_seq_len,
+                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads,
+                     int32_t mask_num_heads, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
+                     float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
                                   target_group_size, dtype, num_context, num_targets);
   if (st != HSTU_OK) return st;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return HSTU_OK;
-  if (!seq_offsets || !aligned4(seq_offsets)) return HSTU_ERR_INVALID_ARG;
+  if (mask_type == HSTU_MASK_CUSTOM && dtype == HSTU_F32) return HSTU_ERR_UNSUPPORTED;
+  if (!seq_offsets || !aligned4(seq_offsets) || (seq_offsets_k && !aligned4(seq_offsets_k)))
+    return HSTU_ERR_INVALID_ARG;
   if (phase & kRun) {
     if (!q || !k || !v || !out) return HSTU_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (rab && !aligned16(rab)))
       return HSTU_ERR_INVALID_ARG;
+    // The user mask comes with mask_type 3 and only then.
+    if ((mask_type == HSTU_MASK_CUSTOM) != (mask != nullptr) || (mask && !aligned16(mask)))
+      return HSTU_ERR_INVALID_ARG;
+    if (rab && rab_num_heads != 1 && rab_num_heads != num_heads_q) return HSTU_ERR_INVALID_ARG;
+    if (mask && mask_num_heads != 1 && mask_num_heads != num_heads_q) return HSTU_ERR_INVALID_ARG;
   }
   const size_t need = hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, dtype);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return HSTU_ERR_WORKSPACE;
@@ -104,13 +112,18 @@ hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, con
   hstu::FwdArgs a{};
   a.dtype = to_internal(dtype);
   a.causal = mask_type == HSTU_MASK_CAUSAL;
+  a.user_mask = mask_type == HSTU_MASK_CUSTOM;
   a.paged = false;
   a.q = q;
   a.k = k;
   a.v = v;
   a.rab = rab;
+  a.mask = mask;
   a.out = out;
   a.seq_offsets = seq_offsets;
+  a.seq_offsets_k = seq_offsets_k;
+  a.rab_heads = rab_num_heads;
+  a.mask_heads = mask_num_heads;
   a.num_context = num_context;
   a.num_targets = num_targets;
   a.batch = batch;
@@ -137,6 +150,7 @@ hstu_status_t paged(int phase, const void* q, const void* k_new, const void* v_n
   hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
                                   target_group_size, dtype, num_context, num_targets);
   if (st != HSTU_OK) return st;
+  if (mask_type == HSTU_MASK_CUSTOM) return HSTU_ERR_UNSUPPORTED;  // the user mask is built for jagged calls
   if (page_size < 0) return HSTU_ERR_INVALID_ARG;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return HSTU_OK;
   if (!page_size_ok(page_size)) return HSTU_ERR_UNSUPPORTED;
@@ -187,35 +201,35 @@ hstu_status_t paged(int phase, const void* q, const void* k_new, const void* v_n
 
 extern "C" {
 
-hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* rab, void* out,
-                       const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
-                       int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                       int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
-                       float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  return jagged(kBoth, q, k, v, rab, out, seq_offsets, num_context, num_targets, batch, max_seq_len, num_heads_q,
-                num_heads_kv, head_dim, mask_type, target_group_size, alpha, out_scale, dtype, workspace,
-                workspace_bytes, stream);
+hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
+                       const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                       const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                       int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
+                       hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
+                       hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return jagged(kBoth, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
+                max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
+                target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
 }
 
-hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
-                            int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                            int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, hstu_dtype_t dtype,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  return jagged(kPlan, nullptr, nullptr, nullptr, nullptr, nullptr, seq_offsets, num_context, num_targets, batch,
-                max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type, target_group_size, 1.0f, 1.0f, dtype,
-                workspace, workspace_bytes, stream);
+hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                            const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                            int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size,
+                            hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return jagged(kPlan, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seq_offsets, seq_offsets_k, num_context,
+                num_targets, batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, 0, 0, mask_type,
+                target_group_size, 1.0f, 1.0f, dtype, workspace, workspace_bytes, stream);
 }
 
-hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, void* out,
-                           const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
-                           int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
-                           float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  return jagged(kRun, q, k, v, rab, out, seq_offsets, num_context, num_targets, batch, max_seq_len, num_heads_q,
-                num_heads_kv, head_dim, mask_type, target_group_size, alpha, out_scale, dtype, workspace,
-                workspace_bytes, stream);
+hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
+                           const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                           const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                           int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
+                           hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
+                           hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return jagged(kRun, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
+                max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
+                target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new, void* out,

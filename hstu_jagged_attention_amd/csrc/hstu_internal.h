@@ -15,12 +15,15 @@ struct FwdArgs {
   DType dtype;
   bool causal;
   bool paged;
+  bool user_mask;  // mask_type 3: the mask tensor decides (causal is false)
   const void* q;
   const void* k;  // jagged: k; paged: k_new
   const void* v;  // jagged: v; paged: v_new
   const void* rab;
+  const void* mask;            // user mask [B, mask_heads, S, S] (user_mask only)
   void* out;
   const int32_t* seq_offsets;  // jagged: [B+1]; paged: new tokens per request [B+1]
+  const int32_t* seq_offsets_k;  // jagged keys [B+1], or NULL (the same as seq_offsets)
   const int32_t* num_context;
   const int32_t* num_targets;
   const void* kv_cache;
@@ -33,6 +36,8 @@ struct FwdArgs {
   int32_t num_heads_q;
   int32_t num_heads_kv;
   int32_t head_dim;
+  int32_t rab_heads;   // 1 (one rab for every head) or num_heads_q
+  int32_t mask_heads;  // 1 or num_heads_q
   int32_t target_group_size;
   float alpha;
   float out_scale;

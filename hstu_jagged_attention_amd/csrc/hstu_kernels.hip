@@ -64,8 +64,10 @@ struct KParams {
   const void* k;
   const void* v;
   const void* rab;
+  const void* mask;   // user mask (mask_type 3), laid out as rab
   void* out;
   const int32_t* seq_offsets;
+  const int32_t* seq_offsets_k;  // jagged keys, or NULL: the queries' offsets
   const int32_t* num_context;
   const int32_t* num_targets;
   const void* kv_cache;
@@ -95,6 +97,8 @@ struct KParams {
   int32_t ps_log2;    // log2(page_size)
   int32_t g;          // target_group_size
   int32_t rab_vec;    // rab rows allow 4-element vector loads
+  int32_t rab_heads;  // 1: one rab (and mask_heads 1: one mask) for every query head
+  int32_t mask_heads;
   float alpha;
   float c_exp;        // -alpha * log2(e)
   float out_mul;      // final scale of O (see the kernels)
@@ -105,9 +109,10 @@ struct KParams {
 // ------------------------------------------------------------------------
 struct Seq {
   int q_tok0;  // row of query 0 in q / out
-  int k_tok0;  // row of key position Lh in k / v (jagged: position 0)
+  int k_tok0;  // row of key position Lh in k / v (paged), of position 0 (jagged)
   int Lq;      // queries of this sequence
-  int Lh;      // absolute position of query 0 (paged history length, else 0)
+  int Lh;      // absolute position of query 0 (paged: history length;
+               // jagged: keys minus queries, 0 when they are equal)
   int L;       // key positions 0 .. L-1
   int H;       // first target position (L - clamped num_targets)
   int nc;      // clamped num_context
@@ -127,6 +132,13 @@ __device__ inline Seq load_seq(const KParams& p, int b, bool causal) {
     const int pg0 = p.page_offsets[b], pg1 = p.page_offsets[b + 1];
     s.page0 = pg0;
     s.Lh = pg1 > pg0 ? ((pg1 - pg0 - 1) << p.ps_log2) + p.last_page_len[b] : 0;
+  } else if (p.seq_offsets_k) {
+    // The queries are the last Lq of the Lk key positions. More queries
+    // than keys is invalid input; the rows past Lk are then left unwritten.
+    const int k0 = p.seq_offsets_k[b], Lk = p.seq_offsets_k[b + 1] - k0;
+    s.k_tok0 = k0;
+    s.Lq = min(s.Lq, max(Lk, 0));
+    s.Lh = max(Lk, 0) - s.Lq;
   }
   s.L = s.Lh + s.Lq;
   int nt = (causal && p.num_targets) ? p.num_targets[b] : 0;
@@ -525,7 +537,9 @@ __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  
 // of the item (each group with its own LDS buffers) and the two partial
 // O tiles are summed through LDS at the end. This halves an item's latency,
 // for work lists too short to fill the chip.
-template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE, int KSP>
+// MSK: the user mask (mask_type 3, no built-in mask): its value m for
+// (i, j) multiplies P, and m == 0 removes the key like the built-in masks do.
+template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE, int KSP, bool MSK = false>
 __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(WPE))) void fwd_kernel(KParams p) {
   using F = Frag<T>;
   using V8 = typename F::v8;
@@ -744,21 +758,26 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-    // Rows past the sequence read the rab of its last row (always in bounds;
-    // their results are never stored).
-    const T* rrow = RAB ? (const T*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + min(q_loc, max(s.Lq - 1, 0))) *
-                                                p.max_seq_len
-                        : nullptr;
-    // rab of the tile at key j0: lane holds row q_loc, keys j0 + 32 jb + 8 a + 4 half + 0..3.
-    // Loaded one step ahead (issued right after the next tile's DMA), so the
-    // step that uses it never waits for memory in the middle.
+    // rab and the user mask are [B, heads, S, S] (heads 1: shared by every
+    // query head), indexed by absolute positions. Rows past the sequence
+    // read its last row (always in bounds; their results are never stored).
+    auto sq_row = [&](const void* base, int heads) -> const T* {
+      const int row = s.Lh + min(q_loc, max(s.Lq - 1, 0));
+      return (const T*)base + ((size_t)(b * heads + (heads == 1 ? 0 : h)) * p.max_seq_len + row) * p.max_seq_len;
+    };
+    const T* rrow = RAB ? sq_row(p.rab, p.rab_heads) : nullptr;
+    const T* mrow = MSK ? sq_row(p.mask, p.mask_heads) : nullptr;
+    // rab (or mask) of the tile at key j0: lane holds row q_loc, keys
+    // j0 + 32 jb + 8 a + 4 half + 0..3. Loaded one step ahead (issued right
+    // after the next tile's DMA), so the step that uses it never waits for
+    // memory in the middle. Keys past the sequence read 0.
     using RabRegs = u32x2_t[NJB][4];
-    auto load_rab = [&](int j0, RabRegs& rv) {
+    auto load_rab = [&](const T* row, int j0, RabRegs& rv) {
       if (j0 + BN <= s.L && p.rab_vec) {  // uniform: whole tile inside the sequence, 8-byte aligned rows
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-          for (int a = 0; a < 4; ++a) rv[jb][a] = *(const u32x2_t*)(rrow + j0 + jb * 32 + 8 * a + 4 * half);
+          for (int a = 0; a < 4; ++a) rv[jb][a] = *(const u32x2_t*)(row + j0 + jb * 32 + 8 * a + 4 * half);
       } else {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
@@ -767,14 +786,15 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
             const int jj = j0 + jb * 32 + 8 * a + 4 * half;
             T t4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) t4[e] = (jj + e < s.L) ? rrow[jj + e] : (T)0.f;
+            for (int e = 0; e < 4; ++e) t4[e] = (jj + e < s.L) ? row[jj + e] : (T)0.f;
             rv[jb][a] = *(const u32x2_t*)t4;
           }
       }
     };
-    RabRegs rv_next;
-    if constexpr (RAB) {
-      if (n_begin + GRP < n_end) load_rab(tile_at(n_begin + GRP) * BN, rv_next);
+    RabRegs rv_next, mv_next;
+    if (n_begin + GRP < n_end) {
+      if constexpr (RAB) load_rab(rrow, tile_at(n_begin + GRP) * BN, rv_next);
+      if constexpr (MSK) load_rab(mrow, tile_at(n_begin + GRP) * BN, mv_next);
     }
     const int G = lane >> 4, sl = lane & 15;
 
@@ -792,13 +812,20 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // The next tile's DMA goes out first: it has a whole step to land;
       // then the next tile's rab (this tile's arrived last step).
       if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
-      RabRegs rv;
+      RabRegs rv, mv;
       if constexpr (RAB) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int a = 0; a < 4; ++a) rv[jb][a] = rv_next[jb][a];
-        if (n + KSP < n_end) load_rab(tile_at(n + KSP) * BN, rv_next);
+        if (n + KSP < n_end) load_rab(rrow, tile_at(n + KSP) * BN, rv_next);
+      }
+      if constexpr (MSK) {
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) mv[jb][a] = mv_next[jb][a];
+        if (n + KSP < n_end) load_rab(mrow, tile_at(n + KSP) * BN, mv_next);
       }
       if (!wave_active || !has_tile) return;
 
@@ -847,18 +874,23 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       V8 pf[NJB][2];
       // Epilogue of element r of block jb: rab, mask (masked tiles), SiLU, round.
       // rab and mask of element r of block jb: y (kept in sacc).
+      // Element r of block jb of a prefetched rab / mask tile, as float.
+      auto sq_val = [&](const RabRegs& rg, int jb, int r) -> float {
+        const uint32_t wd = rg[jb][r / 4][(r % 4) / 2];
+        if constexpr (std::is_same<T, __bf16>::value) {
+          return __builtin_bit_cast(float, (r % 2) ? (wd & 0xffff0000u) : (wd << 16));
+        } else {
+          const T* t2 = (const T*)&wd;
+          return (float)t2[r % 2];
+        }
+      };
       auto epi_pre = [&](auto masked, int jb, int r) -> float {
         float y = sacc[jb][r];
-        if (RAB) {
-          const uint32_t wd = rv[jb][r / 4][(r % 4) / 2];
-          float rab_f;
-          if constexpr (std::is_same<T, __bf16>::value) {
-            rab_f = __builtin_bit_cast(float, (r % 2) ? (wd & 0xffff0000u) : (wd << 16));
-          } else {
-            const T* t2 = (const T*)&wd;
-            rab_f = (float)t2[r % 2];
-          }
-          y = __builtin_fmaf(rab_f, p.c_exp, y);
+        if (RAB) y = __builtin_fmaf(sq_val(rv, jb, r), p.c_exp, y);
+        if constexpr (MSK) {
+          // A zero mask value removes the key: y = +0, so p = 0 exactly.
+          const int keep = sq_val(mv, jb, r) != 0.f ? -1 : 0;
+          y = __builtin_bit_cast(float, __builtin_bit_cast(int, y) & keep);
         }
         if constexpr (decltype(masked)::value) {
           // Masked keys get y = +0 (bitwise AND with the sign-extended
@@ -876,7 +908,8 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       auto epi = [&](auto masked, int jb, int r) {
         const float y = epi_pre(masked, jb, r);
         const float e = __builtin_amdgcn_exp2f(y);
-        const float pv = y * __builtin_amdgcn_rcpf(1.f + e);
+        float pv = y * __builtin_amdgcn_rcpf(1.f + e);
+        if constexpr (MSK) pv *= sq_val(mv, jb, r);
         pf[jb][r / 8][r % 8] = (T)pv;
       };
       // The same for the 16 elements of block jb, one operation at a time
@@ -884,7 +917,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // independent chains, and every result is used EB instructions after
       // it is made.
       auto epi_block = [&](auto masked, int jb) {
-        constexpr int EB = RAB ? 8 : 16;  // elements per pass (rab values hold registers too)
+        constexpr int EB = (RAB || MSK) ? 8 : 16;  // elements per pass (rab / mask values hold registers too)
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += EB) {
           float y[EB], e[EB];
@@ -901,7 +934,11 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
           for (int r = 0; r < EB; ++r) e[r] = __builtin_amdgcn_rcpf(e[r]);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int r = 0; r < EB; ++r) pf[jb][(r0 + r) / 8][(r0 + r) % 8] = (T)(y[r] * e[r]);
+          for (int r = 0; r < EB; ++r) {
+            float pv = y[r] * e[r];
+            if constexpr (MSK) pv *= sq_val(mv, jb, r0 + r);
+            pf[jb][(r0 + r) / 8][(r0 + r) % 8] = (T)pv;
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
@@ -972,7 +1009,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         // MFMAs are independent); the K fragments of group g+1 are read
         // while group g multiplies.
         constexpr int NS = KS * NJB;        // S MFMAs per tile
-        constexpr int GS = RAB ? 1 : 2;     // MFMAs per group (rab prefetch holds registers)
+        constexpr int GS = (RAB || MSK) ? 1 : 2;  // MFMAs per group (rab / mask prefetch holds registers)
         constexpr int NGS = NS / GS;
         static_assert(NS % GS == 0, "S groups");
         auto s_kf = [&](int q) { return k_frag(q % NJB, q / NJB); };  // q-th S MFMA: ks = q / NJB, jb = q % NJB
@@ -1000,7 +1037,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         // O^T operands: groups of GP MFMAs in (jb, m, db) order, V^T
         // fragments one group ahead; group 0 is read during the epilogue.
         constexpr int NP = NJB * 2 * NDB;
-        constexpr int GP = (RAB || NDB < 2) ? 1 : 2;
+        constexpr int GP = (RAB || MSK || NDB < 2) ? 1 : 2;
         constexpr int NGP = NP / GP;
         static_assert(NDB % GP == 0, "PV groups");
         auto p_vf = [&](int q) { return v_frag(q / (2 * NDB), (q / NDB) % 2, q % NDB); };
@@ -1292,7 +1329,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) v
       const int j1 = min(j0 + BN, s.L);
       const bool full = !CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc));
       const float* rrow =
-          RAB ? (const float*)p.rab + ((size_t)(b * p.Hq + h) * p.max_seq_len + q_loc) * p.max_seq_len : nullptr;
+          RAB ? (const float*)p.rab + ((size_t)(b * p.rab_heads + (p.rab_heads == 1 ? 0 : h)) * p.max_seq_len + s.Lh +
+                 q_loc) * p.max_seq_len
+              : nullptr;  // read for rows inside the sequence only
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
@@ -1362,10 +1401,12 @@ int num_cus() {
 using KernelFn = void (*)(KParams);
 
 template <typename T, int D, bool PAGED>
-KernelFn pick16(bool causal, bool rab, bool ksplit) {
+KernelFn pick16(bool causal, bool rab, bool ksplit, bool user_mask) {
   constexpr int BN = D >= 256 ? 32 : 64;
   constexpr int WPE = D >= 256 ? 1 : 2;
   if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE, 1> : fwd_kernel<T, D, BN, false, false, true, WPE, 1>;
+  if (user_mask)
+    return rab ? fwd_kernel<T, D, BN, false, true, false, WPE, 1, true> : fwd_kernel<T, D, BN, false, false, false, WPE, 1, true>;
   if constexpr (BN == 64) {
     if (ksplit) {
       if (causal) return rab ? fwd_kernel<T, D, BN, true, true, false, WPE, 2> : fwd_kernel<T, D, BN, true, false, false, WPE, 2>;
@@ -1384,28 +1425,30 @@ KernelFn pick32(bool causal, bool rab) {
   return rab ? fwd_kernel_f32<D, BN, false, true, false> : fwd_kernel_f32<D, BN, false, false, false>;
 }
 
-// ksplit: use the 8-wave key-split kernel (16-bit, head_dim <= 128, jagged).
+// ksplit: use the 8-wave key-split kernel (16-bit, head_dim <= 128, jagged,
+// built-in masks). user_mask: mask_type 3 (16-bit jagged only).
 // On return, *wgs_per_cu and *threads give the launch shape.
 template <bool PAGED>
-KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, int* wgs_per_cu, int* threads) {
-  ksplit = ksplit && !PAGED && dt != DType::F32 && D <= 128;
+KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, bool user_mask, int* wgs_per_cu, int* threads) {
+  ksplit = ksplit && !PAGED && dt != DType::F32 && D <= 128 && !user_mask;
+  if (user_mask && (PAGED || dt == DType::F32)) return nullptr;
   *wgs_per_cu = ksplit ? 1 : ((dt == DType::F32 || D >= 256) ? 1 : 2);
   *threads = ksplit ? 2 * kThreads : kThreads;
   switch (dt) {
     case DType::BF16:
       switch (D) {
-        case 32: return pick16<__bf16, 32, PAGED>(causal, rab, ksplit);
-        case 64: return pick16<__bf16, 64, PAGED>(causal, rab, ksplit);
-        case 128: return pick16<__bf16, 128, PAGED>(causal, rab, ksplit);
-        case 256: return pick16<__bf16, 256, PAGED>(causal, rab, ksplit);
+        case 32: return pick16<__bf16, 32, PAGED>(causal, rab, ksplit, user_mask);
+        case 64: return pick16<__bf16, 64, PAGED>(causal, rab, ksplit, user_mask);
+        case 128: return pick16<__bf16, 128, PAGED>(causal, rab, ksplit, user_mask);
+        case 256: return pick16<__bf16, 256, PAGED>(causal, rab, ksplit, user_mask);
       }
       break;
     case DType::F16:
       switch (D) {
-        case 32: return pick16<_Float16, 32, PAGED>(causal, rab, ksplit);
-        case 64: return pick16<_Float16, 64, PAGED>(causal, rab, ksplit);
-        case 128: return pick16<_Float16, 128, PAGED>(causal, rab, ksplit);
-        case 256: return pick16<_Float16, 256, PAGED>(causal, rab, ksplit);
+        case 32: return pick16<_Float16, 32, PAGED>(causal, rab, ksplit, user_mask);
+        case 64: return pick16<_Float16, 64, PAGED>(causal, rab, ksplit, user_mask);
+        case 128: return pick16<_Float16, 128, PAGED>(causal, rab, ksplit, user_mask);
+        case 256: return pick16<_Float16, 256, PAGED>(causal, rab, ksplit, user_mask);
       }
       break;
     case DType::F32:
@@ -1501,6 +1544,10 @@ KParams make_params(const FwdArgs& a) {
   p.k = a.k;
   p.v = a.v;
   p.rab = a.rab;
+  p.mask = a.user_mask ? a.mask : nullptr;
+  p.seq_offsets_k = a.paged ? nullptr : a.seq_offsets_k;
+  p.rab_heads = a.rab_heads == 1 ? 1 : a.num_heads_q;
+  p.mask_heads = a.mask_heads == 1 ? 1 : a.num_heads_q;
   p.out = a.out;
   p.seq_offsets = a.seq_offsets;
   p.num_context = a.num_context;
@@ -1579,8 +1626,9 @@ hipError_t launch_run(const FwdArgs& a) {
   // kernel: one 8-wave workgroup per CU, each item twice as fast.
   const bool ksplit = upper <= num_cus();
   int per_cu = 2, threads = kThreads;
-  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, false, &per_cu, &threads)
-                        : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, ksplit, &per_cu, &threads);
+  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, false, false, &per_cu, &threads)
+                        : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, ksplit, a.user_mask, &per_cu,
+                                      &threads);
   if (!fn) return hipErrorInvalidValue;
   const long long cap = (long long)num_cus() * per_cu;
   const int grid = (int)(upper < cap ? upper : cap);

@@ -67,18 +67,48 @@ def pairs_paged(history_lengths: Sequence[int], new_lengths: Sequence[int], num_
     return total
 
 
+def pairs_delta(key_lengths: Sequence[int], query_lengths: Sequence[int], num_context: Optional[Sequence[int]],
+                num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int) -> int:
+    """Different Q and K lengths: the queries are the last Lq of Lk
+    positions, so only those rows count (ONE query head)."""
+    lk = np.asarray(key_lengths, dtype=np.int64)
+    lq = np.asarray(query_lengths, dtype=np.int64)
+    return pairs_paged(lk - lq, lq, num_context, num_targets, target_group_size, mask_type)
+
+
+def user_mask_counts(mask: np.ndarray, lengths: Sequence[int], num_heads_q: int, rab_heads: int = 0):
+    """User mask (mask_type 3) [B, Hm, S, S]: returns (visible pairs summed
+    over all query heads, distinct rab entries those pairs read when a rab
+    with rab_heads heads is given). A pair is visible where the mask value
+    inside the sequence is non-zero."""
+    total, rab_entries = 0, 0
+    Hm = mask.shape[1]
+    for b, L in enumerate(lengths):
+        L = int(L)
+        nz = mask[b, :, :L, :L] != 0  # [Hm, L, L]
+        per_head = nz.reshape(Hm, -1).sum(axis=1)
+        total += int(per_head.sum()) * (num_heads_q // Hm)
+        if rab_heads == 1:
+            rab_entries += int(nz.any(axis=0).sum())
+        elif rab_heads:
+            rab_entries += int(per_head.sum()) * (num_heads_q // Hm)
+    return total, rab_entries
+
+
 def effective_flops(pairs_one_head: int, num_heads_q: int, head_dim: int) -> float:
     return 4.0 * head_dim * float(pairs_one_head) * num_heads_q
 
 
 def algorithmic_bytes_jagged(T: int, num_heads_q: int, num_heads_kv: int, head_dim: int, elem_bytes: int,
-                             rab_pairs_one_head: int = 0) -> float:
-    """Compulsory HBM bytes: Q and O once, K and V once, rab only for the
-    visible pairs (the method never reads masked rab)."""
+                             rab_pairs_one_head: int = 0, Tk: Optional[int] = None, extra_bytes: float = 0.0) -> float:
+    """Compulsory HBM bytes: Q and O once (T query rows), K and V once (Tk
+    key rows, default T), rab only for the visible pairs (the method never
+    reads masked rab), plus extra_bytes (a user mask, whose every entry
+    inside the sequences is read once per mask head)."""
     qo = 2.0 * T * num_heads_q * head_dim * elem_bytes
-    kv = 2.0 * T * num_heads_kv * head_dim * elem_bytes
+    kv = 2.0 * (T if Tk is None else Tk) * num_heads_kv * head_dim * elem_bytes
     rab = float(rab_pairs_one_head) * num_heads_q * elem_bytes
-    return qo + kv + rab
+    return qo + kv + rab + extra_bytes
 
 
 def algorithmic_bytes_paged(Tq: int, history_tokens: int, num_heads_q: int, num_heads_kv: int, head_dim: int,

@@ -17,8 +17,12 @@
  *
  * Masks (the page's mask_type codes): HSTU_MASK_CAUSAL (0) is the built-in
  * lower-triangular mask with context and targets; HSTU_MASK_NONE (2) is the
- * bidirectional case. Codes 1 (upper triangular, unsupported by the page
- * itself) and 3 (user mask tensor) return HSTU_ERR_UNSUPPORTED.
+ * bidirectional case; HSTU_MASK_CUSTOM (3) takes the user's mask tensor
+ * (the table's mask input, [B, N, S, S] in the dtype of q): every key of
+ * the sequence is a candidate, the mask value m for (i, j) multiplies P,
+ * and m == 0 removes the key entirely (it contributes exactly zero whatever
+ * its score, as with the built-in masks). Code 1 (upper triangular, which
+ * the page itself does not support) returns HSTU_ERR_UNSUPPORTED.
  * For HSTU_MASK_CAUSAL, per sequence of length L with nc = num_context[b],
  * nt = num_targets[b] (0 when the array is NULL) and g = target_group_size:
  * clamp nt to [0, L], H = L - nt, clamp nc to [0, H]. Key j < H is visible to
@@ -63,7 +67,7 @@ typedef enum {
 
 typedef enum { HSTU_F32 = 0, HSTU_F16 = 1, HSTU_BF16 = 2 } hstu_dtype_t;
 
-typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2 } hstu_mask_t;
+typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2, HSTU_MASK_CUSTOM = 3 } hstu_mask_t;
 
 /* Supported sizes: head_dim in {32, 64, 128, 256} for f16/bf16 and
  * {32, 64, 128} for f32 (the page allows multiples of 16 up to 512);
@@ -78,33 +82,48 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
                                int32_t head_dim, hstu_dtype_t dtype);
 
 /*
- * Jagged forward (the page's "jagged" layout, seq_offsets_q == seq_offsets_k).
- *  q           [T, num_heads_q,  head_dim]  dtype   (T = seq_offsets[batch])
- *  k, v        [T, num_heads_kv, head_dim]  dtype
- *  rab         [batch, num_heads_q, max_seq_len, max_seq_len] dtype, or NULL.
- *              Indexed by positions local to the sequence; only visible
- *              (i, j) inside the sequence are read.
- *  out         [T, num_heads_q, head_dim]   dtype (written for every token)
- *  seq_offsets [batch + 1] int32, non-decreasing, seq_offsets[0] == 0.
+ * Jagged forward (the page's "jagged" layout: q/k/v [T, N, D] addressed by
+ * seq_offsets, and seq_offsets_k with is_delta_qk when Q and K lengths
+ * differ).
+ *  q             [Tq, num_heads_q,  head_dim]  dtype  (Tq = seq_offsets[batch])
+ *  k, v          [Tk, num_heads_kv, head_dim]  dtype  (Tk = seq_offsets_k[batch])
+ *  rab           [batch, rab_num_heads, max_seq_len, max_seq_len] dtype, or
+ *                NULL. rab_num_heads is num_heads_q or 1 (the page's rab
+ *                broadcast [b, 1, s, s]: one rab for every head). Indexed by
+ *                absolute positions (i, j) within the sequence; only (i, j)
+ *                the mask does not remove are read.
+ *  mask          [batch, mask_num_heads, max_seq_len, max_seq_len] dtype with
+ *                HSTU_MASK_CUSTOM, else NULL. mask_num_heads is num_heads_q or
+ *                1; indexed as rab. f16/bf16 only.
+ *  out           [Tq, num_heads_q, head_dim]   dtype (written for every query)
+ *  seq_offsets   [batch + 1] int32, non-decreasing, seq_offsets[0] == 0.
+ *  seq_offsets_k [batch + 1] int32, or NULL (keys = queries). When given, the
+ *                Lq = seq_offsets[b+1] - seq_offsets[b] queries of sequence b
+ *                are its last Lq positions among Lk = seq_offsets_k[b+1] -
+ *                seq_offsets_k[b] keys (query t at absolute position
+ *                Lk - Lq + t); Lq <= Lk is the caller's duty (queries past Lk
+ *                are left unwritten). Masks and rab use absolute positions.
  *  num_context, num_targets [batch] int32, or NULL (= all zero). Must be
- *              NULL with HSTU_MASK_NONE.
+ *                NULL unless mask_type is HSTU_MASK_CAUSAL.
  *  target_group_size >= 0 (0 = no target mask).
- *  alpha       scale applied to (Q.K^T + rab) before SiLU.
- *  out_scale   scale applied after SiLU (the page's silu_scale; its default
- *              is 1/max_seq_len, applied by the Python binding).
+ *  alpha         scale applied to (Q.K^T + rab) before SiLU.
+ *  out_scale     scale applied after SiLU (the page's silu_scale; its default
+ *                is 1/max_seq_len, applied by the Python binding).
  * Errors: HSTU_ERR_INVALID_ARG for negative sizes, num_heads_q not a
  * multiple of num_heads_kv, null q/k/v/out/seq_offsets, pointers not 16-byte
- * aligned, num_context/num_targets with HSTU_MASK_NONE, target_group_size <
- * 0; HSTU_ERR_UNSUPPORTED for other mask codes, head_dim or dtype;
- * HSTU_ERR_WORKSPACE if workspace_bytes is too small; HSTU_ERR_HIP if a
- * launch fails.
+ * aligned, num_context/num_targets with a mask other than causal, a mask
+ * without HSTU_MASK_CUSTOM or HSTU_MASK_CUSTOM without a mask, rab or mask
+ * head counts other than 1 and num_heads_q, target_group_size < 0 or an
+ * unknown mask code; HSTU_ERR_UNSUPPORTED for mask code 1, head_dim, dtype,
+ * or HSTU_MASK_CUSTOM in f32; HSTU_ERR_WORKSPACE if workspace_bytes is too
+ * small; HSTU_ERR_HIP if a launch fails.
  */
-hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* rab, void* out,
-                       const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
-                       int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                       int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
-                       float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                       void* stream /* hipStream_t */);
+hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
+                       const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                       const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                       int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
+                       hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
+                       hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /*
  * hstu_fwd in two steps, for callers that time or reuse them separately
@@ -112,29 +131,31 @@ hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* 
  * stacked layers over the same batch can plan once and run many times).
  *
  * hstu_fwd_plan: the tile scheduler alone. It reads seq_offsets,
- * num_context and num_targets on the device and writes into `workspace` a
- * work list of (sequence, query tile) items, longest first (by the number of
- * key tiles not fully masked), plus the queue counters the run consumes.
- * Arguments and errors as hstu_fwd (q, k, v, rab, out are not needed).
+ * seq_offsets_k, num_context and num_targets on the device and writes into
+ * `workspace` a work list of (sequence, query tile) items, longest first (by
+ * the number of key tiles not fully masked), plus the queue counters the run
+ * consumes. Arguments and errors as hstu_fwd (q, k, v, rab, mask and out are
+ * not needed).
  *
  * hstu_fwd_run: the fused forward kernel alone, consuming the plan held in
  * `workspace`. The caller guarantees that the plan was made with the same
- * seq_offsets contents, num_context, num_targets, batch, max_seq_len, head
- * counts, head_dim, mask_type, target_group_size and dtype, and that no
- * other call uses the workspace between the plan and the run. A run leaves
- * the plan intact, so further runs may follow. hstu_fwd == plan + run.
+ * seq_offsets / seq_offsets_k contents, num_context, num_targets, batch,
+ * max_seq_len, head counts, head_dim, mask_type, target_group_size and
+ * dtype, and that no other call uses the workspace between the plan and the
+ * run. A run leaves the plan intact, so further runs may follow.
+ * hstu_fwd == plan + run.
  */
-hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
-                            int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                            int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, hstu_dtype_t dtype,
-                            void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                            const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                            int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size,
+                            hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
-hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, void* out,
-                           const int32_t* seq_offsets, const int32_t* num_context, const int32_t* num_targets,
-                           int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
-                           float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                           void* stream /* hipStream_t */);
+hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
+                           const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                           const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                           int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
+                           hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
+                           hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
 /*
  * Workspace bytes hstu_fwd_paged needs. max_seq_len bounds history + new
@@ -158,9 +179,9 @@ size_t hstu_fwd_paged_workspace_size(int32_t batch, int32_t page_size, int32_t m
  *                 it owns no page).
  * Query t of request b sits at absolute position history_len + t of a
  * sequence of history_len + Tq_b tokens; the mask (num_context, num_targets,
- * target_group_size) is applied on those absolute positions. No rab.
- * Errors as hstu_fwd, plus HSTU_ERR_UNSUPPORTED for page_size outside
- * {32, 64, 128, 256}.
+ * target_group_size) is applied on those absolute positions. No rab and no
+ * user mask. Errors as hstu_fwd, plus HSTU_ERR_UNSUPPORTED for page_size
+ * outside {32, 64, 128, 256} and for HSTU_MASK_CUSTOM.
  */
 hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new, void* out,
                              const int32_t* seq_offsets_q, const void* kv_cache, const int32_t* page_offsets,

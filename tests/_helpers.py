@@ -32,9 +32,11 @@ def gpu_device():
 
 
 def run_jagged(c, dev, out=None, workspace=None, **over) -> torch.Tensor:
-    kw = dict(rab=None if c.rab is None else c.rab.to(dev), num_context=c.num_context, num_targets=c.num_targets,
-              max_seq_len=c.max_seq_len, mask_type=c.mask_type, target_group_size=c.target_group_size,
-              alpha=c.alpha, out_scale=c.out_scale, out=out, workspace=workspace)
+    kw = dict(rab=None if c.rab is None else c.rab.to(dev), mask=None if c.mask is None else c.mask.to(dev),
+              seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
+              num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
+              target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale, out=out,
+              workspace=workspace)
     kw.update(over)
     return hj.hstu_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets), **kw)
 
@@ -51,6 +53,7 @@ def run_paged(pc, dev, **over) -> torch.Tensor:
 
 def oracle_jagged(c, rows=None) -> np.ndarray:
     return oracle.hstu_fwd(f64(c.q), f64(c.k), f64(c.v), c.seq_offsets, rab=None if c.rab is None else f64(c.rab),
+                           mask=None if c.mask is None else f64(c.mask), seq_offsets_k=c.seq_offsets_k,
                            num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
                            mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
                            out_scale=c.out_scale, rows=rows)
@@ -62,10 +65,14 @@ def oracle_jagged_sampled(c, picks):
     others), so the oracle never needs the whole batch in float64.
     Returns {b: (global token rows, heads, values [n, D])}."""
     res = {}
+    koff = c.seq_offsets if c.seq_offsets_k is None else c.seq_offsets_k
     for b, rows in picks.items():
         s0, s1 = int(c.seq_offsets[b]), int(c.seq_offsets[b + 1])
+        k0, k1 = int(koff[b]), int(koff[b + 1])
         rab = None if c.rab is None else f64(c.rab[b:b + 1])
-        vals = oracle.hstu_fwd(f64(c.q[s0:s1]), f64(c.k[s0:s1]), f64(c.v[s0:s1]), [0, s1 - s0], rab=rab,
+        mask = None if c.mask is None else f64(c.mask[b:b + 1])
+        vals = oracle.hstu_fwd(f64(c.q[s0:s1]), f64(c.k[k0:k1]), f64(c.v[k0:k1]), [0, s1 - s0], rab=rab, mask=mask,
+                               seq_offsets_k=None if c.seq_offsets_k is None else [0, k1 - k0],
                                num_context=None if c.num_context is None else c.num_context[b:b + 1],
                                num_targets=None if c.num_targets is None else c.num_targets[b:b + 1],
                                max_seq_len=c.max_seq_len, mask_type=c.mask_type,

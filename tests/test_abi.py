@@ -47,12 +47,13 @@ def test_status_strings(lib):
 
 
 def fwd(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, rab=None, out=FAKE, off=FAKE, nc=None, nt=None, B=2, S=128, Hq=4, Hk=2, D=128,
-             mask=0, g=0, alpha=1.0, osc=1.0, dt=BF16, ws=FAKE, wsb=1 << 20, stream=None)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, rab=None, umask=None, out=FAKE, off=FAKE, offk=None, nc=None, nt=None, B=2,
+             S=128, Hq=4, Hk=2, D=128, rab_h=4, mask_h=4, mask=0, g=0, alpha=1.0, osc=1.0, dt=BF16, ws=FAKE,
+             wsb=1 << 30, stream=None)
     a.update(kw)
-    return lib.hstu_fwd(a["q"], a["k"], a["v"], a["rab"], a["out"], a["off"], a["nc"], a["nt"], a["B"], a["S"],
-                        a["Hq"], a["Hk"], a["D"], a["mask"], a["g"], a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"],
-                        a["stream"])
+    return lib.hstu_fwd(a["q"], a["k"], a["v"], a["rab"], a["umask"], a["out"], a["off"], a["offk"], a["nc"],
+                        a["nt"], a["B"], a["S"], a["Hq"], a["Hk"], a["D"], a["rab_h"], a["mask_h"], a["mask"], a["g"],
+                        a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 def paged(lib, **kw):
@@ -81,7 +82,14 @@ def test_empty_inputs_are_a_noop(lib):
     (dict(S=0), INVAL),
     (dict(S=20481), INVAL),
     (dict(mask=1), UNSUP),                    # upper triangular: unsupported by the page itself
-    (dict(mask=3), UNSUP),                    # user mask tensor
+    (dict(mask=3), INVAL),                    # user mask code without the mask tensor
+    (dict(umask=FAKE), INVAL),                # mask tensor without the user mask code
+    (dict(mask=3, umask=FAKE, nt=FAKE), INVAL),  # built-in mask inputs with the user mask
+    (dict(mask=3, umask=FAKE + 4), INVAL),    # not 16-byte aligned
+    (dict(mask=3, umask=FAKE, mask_h=2), INVAL),  # mask heads neither 1 nor num_heads_q
+    (dict(mask=3, umask=FAKE, D=64, dt=F32), UNSUP),  # the user mask is built for f16/bf16
+    (dict(rab=FAKE, rab_h=3), INVAL),         # rab heads neither 1 nor num_heads_q
+    (dict(offk=FAKE + 2), INVAL),
     (dict(mask=7), INVAL),
     (dict(D=48), UNSUP),
     (dict(D=256, dt=F32), UNSUP),

@@ -273,3 +273,77 @@ def test_page_running_case_shape(dev):
     ref = oracle.hstu_fwd(f64(q[:256]), f64(k[:256]), f64(v[:256]), [0, 128, 256], max_seq_len=256, mask_type=CAUSAL,
                           out_scale=1.0 / 256)
     assert_parity(out[:256], ref, "f16", "page running case")
+
+
+# ------------------------------------------------------------ user mask, rab broadcast, delta-QK
+CUSTOM = wl.MASK_CUSTOM
+NEXT = [
+    # (name, key lengths, query lengths or None, Hq, Hk, D, dtype, mask, nc, nt, g, rab_std, rab_heads,
+    #  mask_keep, mask_heads, S)
+    ("user_mask_bf16", [200, 77, 300], None, 4, 4, 128, "bf16", CUSTOM, None, None, 0, None, None, 0.5, None, None),
+    ("user_mask_rab_bcast_f16", [130, 64, 257], None, 4, 2, 128, "f16", CUSTOM, None, None, 0, 0.1, 1, 0.3, 1, None),
+    ("user_mask_gqa_d64_odd_S", [90, 150], None, 6, 2, 64, "bf16", CUSTOM, None, None, 0, 0.5, None, 0.7, 1, 151),
+    ("user_mask_d256", [70, 130], None, 2, 2, 256, "bf16", CUSTOM, None, None, 0, 0.1, 2, 0.5, 2, None),
+    ("user_mask_d32_empty_seq", [0, 40, 1], None, 2, 2, 32, "f16", CUSTOM, None, None, 0, None, None, 0.5, None, None),
+    ("user_mask_many_seqs", [60 + 7 * i for i in range(40)], None, 4, 4, 128, "bf16", CUSTOM, None, None, 0, 0.1, 1,
+     0.5, None, None),
+    ("rab_bcast_causal", [150, 270], None, 4, 4, 128, "bf16", CAUSAL, (0, 8), (1, 16), 1, 0.5, 1, None, None, None),
+    ("rab_bcast_gqa_f16", [150, 270], None, 8, 2, 128, "f16", CAUSAL, None, (1, 16), 1, 0.5, 1, None, None, None),
+    ("delta_causal_targets", [600, 333, 1030], [40, 333, 1], 4, 4, 128, "bf16", CAUSAL, None, [40, 333, 1], 1, None,
+     None, None, None, None),
+    ("delta_ctx_rab", [500, 260], [70, 9], 4, 2, 128, "f16", CAUSAL, (0, 20), (1, 30), 2, 0.1, None, None, None, None),
+    ("delta_none_gqa", [300, 129], [64, 129], 8, 2, 64, "bf16", NONE, None, None, 0, None, None, None, None, None),
+    ("delta_d256", [300, 129], [64, 100], 2, 2, 256, "bf16", CAUSAL, None, (1, 30), 1, 0.1, 1, None, None, None),
+    ("delta_f32_rab_bcast", [200, 90], [33, 90], 2, 2, 64, "f32", CAUSAL, None, (1, 20), 1, 0.5, 1, None, None, None),
+    ("delta_user_mask", [400, 150], [50, 150], 4, 4, 128, "bf16", CUSTOM, None, None, 0, 0.1, 1, 0.5, 4, None),
+    ("delta_many_seqs", [500 + 13 * i for i in range(48)], [1 + (5 * i) % 64 for i in range(48)], 4, 4, 128, "bf16",
+     CAUSAL, None, [1 + (5 * i) % 64 for i in range(48)], 1, None, None, None, None, None),
+]
+
+
+@pytest.mark.parametrize("case", NEXT, ids=[e[0] for e in NEXT])
+def test_user_mask_rab_broadcast_delta_qk(dev, case):
+    """The table's user mask (mask_type 3), rab broadcast [b, 1, s, s] and
+    different Q/K lengths (seq_offsets_k), element by element against the
+    oracle; spans several tiles, ragged tails, the direct and work-list
+    launch modes, head dims 32..256 and the f32 path for delta-QK."""
+    name, lk, lq, Hq, Hk, D, dt, mask, nc, nt, g, rab_std, rab_h, keep, mask_h, S = case
+    seed = zlib.crc32(name.encode()) & 0xffff
+    say(name, "seed", seed, "keys", lk, "queries", lq)
+    c = wl.jagged_case(seed, lk, Hq, Hk, D, dt, mask_type=mask, num_context=nc, num_targets=nt, target_group_size=g,
+                       rab_std=rab_std, rab_heads=rab_h, mask_keep=keep, mask_heads=mask_h, max_seq_len=S,
+                       q_lengths=lq, name=name)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), dt, name)
+
+
+def test_user_mask_zero_removes_nan_rab_on_gpu(dev):
+    """Zero user-mask entries contribute exactly zero even where rab is NaN:
+    the output equals the run with those rab entries finite, bit for bit."""
+    c = wl.jagged_case(91, [150, 64, 200], 4, 4, 128, "bf16", mask_type=CUSTOM, rab_std=0.1, mask_keep=0.5,
+                       name="nan_under_zero_mask")
+    say("nan_under_zero_mask")
+    clean = run_jagged(c, dev).cpu()
+    rab = c.rab.clone()
+    rab[torch.nan_to_num(c.mask.float(), nan=1.0) == 0] = float("nan")
+    got = run_jagged(c, dev, rab=rab.to(dev)).cpu()
+    assert torch.isfinite(got.float()).all()
+    assert torch.equal(got, clean)
+
+
+@pytest.mark.parametrize("name", ["bf16_custom_mask", "bf16_delta_qk"])
+def test_next_workloads_reduced_batch(dev, name):
+    c = wl.WORKLOADS[name](batch=3)
+    say(name, "batch 3", c.lengths.tolist(), c.key_lengths.tolist())
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), c.dtype, name)
+
+
+@pytest.mark.parametrize("name", ["bf16_custom_mask", "bf16_delta_qk"])
+def test_next_workloads_full_size_sampled(dev, name):
+    c = wl.WORKLOADS[name]()
+    say(name, "full size: B", c.batch, "Tq", int(c.seq_offsets[-1]))
+    got = run_jagged(c, dev).cpu()
+    ref = oracle_jagged_sampled(c, _picks(c))
+    for b, (toks, heads, vals) in ref.items():
+        assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, c.dtype, f"{name} seq {b}")
