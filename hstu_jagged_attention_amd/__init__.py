@@ -65,7 +65,7 @@ def load_library(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     E = ctypes.c_int
-    lib.hstu_fwd_workspace_size.argtypes = [I32, I32, I32, I32, I32, E]
+    lib.hstu_fwd_workspace_size.argtypes = [I32, I32, I32, I32, I32, E, I32]
     lib.hstu_fwd_workspace_size.restype = SZ
     lib.hstu_fwd_paged_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, E]
     lib.hstu_fwd_paged_workspace_size.restype = SZ
@@ -93,9 +93,9 @@ def status_string(status: int) -> str:
 
 
 def hstu_fwd_workspace_size(batch: int, max_seq_len: int, num_heads_q: int, num_heads_kv: int, head_dim: int,
-                            dtype: torch.dtype) -> int:
+                            dtype: torch.dtype, is_delta_qk: bool = False) -> int:
     return int(load_library().hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim,
-                                                       DTYPE_CODES[dtype]))
+                                                       DTYPE_CODES[dtype], int(bool(is_delta_qk))))
 
 
 def hstu_fwd_paged_workspace_size(batch: int, page_size: int, max_seq_len: int, num_heads_q: int, num_heads_kv: int,
@@ -223,7 +223,7 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
         _dev_tensor(out, "out", dtype, device)
     Hq, Hk, D = int(q.shape[1]), int(k.shape[1]), int(q.shape[2])
     code = DTYPE_CODES[dtype]
-    need = int(lib.hstu_fwd_workspace_size(B, max_seq_len, Hq, Hk, D, code))
+    need = int(lib.hstu_fwd_workspace_size(B, max_seq_len, Hq, Hk, D, code, 0 if offk is None else 1))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     wsb = workspace.numel() * workspace.element_size()

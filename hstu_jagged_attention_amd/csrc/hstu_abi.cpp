@@ -53,11 +53,12 @@ hstu_status_t check_common(int32_t batch, int32_t max_seq_len, int32_t hq, int32
 extern "C" {
 
 size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                               int32_t head_dim, hstu_dtype_t dtype) {
+                               int32_t head_dim, hstu_dtype_t dtype, int32_t is_delta_qk) {
   if (batch < 0 || max_seq_len < 0 || num_heads_q < 0 || num_heads_kv < 0 || head_dim < 0) return 0;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return 256;
   if (num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
-  return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype), false);
+  return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype),
+                                   is_delta_qk != 0);
 }
 
 size_t hstu_fwd_paged_workspace_size(int32_t batch, int32_t page_size, int32_t max_seq_len, int32_t num_heads_q,
@@ -106,7 +107,8 @@ hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, con
     if (rab && rab_num_heads != 1 && rab_num_heads != num_heads_q) return HSTU_ERR_INVALID_ARG;
     if (mask && mask_num_heads != 1 && mask_num_heads != num_heads_q) return HSTU_ERR_INVALID_ARG;
   }
-  const size_t need = hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, dtype);
+  const size_t need =
+      hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, dtype, seq_offsets_k ? 1 : 0);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return HSTU_ERR_WORKSPACE;
 
   hstu::FwdArgs a{};

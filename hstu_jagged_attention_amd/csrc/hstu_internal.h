@@ -47,10 +47,11 @@ struct FwdArgs {
 };
 
 // Bytes of workspace a launch needs: work list, queue counters and, when
-// the launch may split long items over the key range, the split list and
+// the launch may split long items over the key range (split_keys: paged
+// calls and jagged calls with their own key offsets), the split list and
 // the fp32 partial sums.
 size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, DType dtype, bool paged);
+                           int32_t head_dim, DType dtype, bool split_keys);
 
 // Enqueues the planner on args.stream: it writes the work list into the
 // workspace and zeroes the work-queue counters.

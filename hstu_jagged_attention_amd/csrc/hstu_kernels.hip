@@ -1498,27 +1498,23 @@ struct WsLayout {
 
 constexpr int kSplitUnits = 1024;  // (slot, head group) pairs of partial sums
 
-// Key-range splitting is used by the paged variant (few new-token queries
-// against long cached histories). For jagged batches the fixed cost of each
-// extra chunk (queue pop, sequence and Q loads, partial sums) outweighed the
-// shorter critical path on the measured workloads, so they are not split.
-bool use_split(int32_t batch, int n_qt_max, int n_hg, bool paged, DType dtype) {
-  if (dtype == DType::F32) return false;
-  (void)batch;
-  (void)n_qt_max;
-  (void)n_hg;
-  return paged;
-}
+// Key-range splitting is used when few queries meet long key ranges: the
+// paged variant (new tokens against cached histories) and jagged calls with
+// their own key offsets. For jagged batches whose queries are the whole
+// sequence, the fixed cost of each extra chunk (queue pop, sequence and Q
+// loads, partial sums, the reduction launch) outweighed the shorter critical
+// path on the measured workloads, so they are not split.
+bool use_split(bool split_keys, DType dtype) { return split_keys && dtype != DType::F32; }
 
 WsLayout ws_layout(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                   DType dtype, bool paged) {
+                   DType dtype, bool split_keys) {
   WsLayout w{};
   const int group = num_heads_q / num_heads_kv;
   const int hpw_log2 = heads_per_wg_log2(group);
   const int bm = kRowsPerWave * (kWaves >> hpw_log2);
   w.n_hg = num_heads_q >> hpw_log2;
   w.n_qt_max = (max_q_len + bm - 1) / bm;
-  w.split_slots = use_split(batch, w.n_qt_max, w.n_hg, paged, dtype) ? max(2, kSplitUnits / w.n_hg) : 0;
+  w.split_slots = use_split(split_keys, dtype) ? max(2, kSplitUnits / w.n_hg) : 0;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t entries = (size_t)batch * w.n_qt_max + w.split_slots;
   w.items = kHeaderBytes;
@@ -1531,9 +1527,9 @@ WsLayout ws_layout(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_
 }  // namespace
 
 size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, DType dtype, bool paged) {
+                           int32_t head_dim, DType dtype, bool split_keys) {
   if (batch < 0 || max_q_len < 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return 0;
-  return ws_layout(batch, max_q_len, num_heads_q, num_heads_kv, head_dim, dtype, paged).total;
+  return ws_layout(batch, max_q_len, num_heads_q, num_heads_kv, head_dim, dtype, split_keys).total;
 }
 
 namespace {
@@ -1556,7 +1552,8 @@ KParams make_params(const FwdArgs& a) {
   p.page_offsets = a.page_offsets;
   p.page_ids = a.page_ids;
   p.last_page_len = a.last_page_len;
-  const WsLayout w = ws_layout(a.batch, a.max_seq_len, a.num_heads_q, a.num_heads_kv, a.head_dim, a.dtype, a.paged);
+  const WsLayout w = ws_layout(a.batch, a.max_seq_len, a.num_heads_q, a.num_heads_kv, a.head_dim, a.dtype,
+                               a.paged || a.seq_offsets_k != nullptr);
   char* ws = (char*)a.workspace;
   p.n_items = (int32_t*)ws;
   p.counter = (int32_t*)(ws + 64);

@@ -76,10 +76,13 @@ typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2, HSTU_MASK_CUSTOM = 3 } 
 
 /*
  * Workspace bytes hstu_fwd needs for these sizes (the work list of the tile
- * scheduler and its queue counters). Returns 0 for invalid sizes.
+ * scheduler and its queue counters; with is_delta_qk != 0, the page's flag
+ * for different Q and K lengths, i.e. calls that pass seq_offsets_k, also the
+ * fp32 partial sums of items split over the key range). Returns 0 for
+ * invalid sizes.
  */
 size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv,
-                               int32_t head_dim, hstu_dtype_t dtype);
+                               int32_t head_dim, hstu_dtype_t dtype, int32_t is_delta_qk);
 
 /*
  * Jagged forward (the page's "jagged" layout: q/k/v [T, N, D] addressed by

@@ -90,6 +90,7 @@ def test_empty_inputs_are_a_noop(lib):
     (dict(mask=3, umask=FAKE, D=64, dt=F32), UNSUP),  # the user mask is built for f16/bf16
     (dict(rab=FAKE, rab_h=3), INVAL),         # rab heads neither 1 nor num_heads_q
     (dict(offk=FAKE + 2), INVAL),
+    (dict(offk=FAKE, wsb=1 << 20), WS),       # key offsets need the key-split partial sums
     (dict(mask=7), INVAL),
     (dict(D=48), UNSUP),
     (dict(D=256, dt=F32), UNSUP),
@@ -127,8 +128,11 @@ def test_workspace_sizes(lib):
     small = hj.hstu_fwd_workspace_size(8, 1024, 4, 4, 128, __import__("torch").bfloat16)
     big = hj.hstu_fwd_workspace_size(8, 4096, 4, 4, 128, __import__("torch").bfloat16)
     assert 0 < small < big
-    assert lib.hstu_fwd_workspace_size(2, 128, 4, 3, 128, BF16) == 0
-    assert lib.hstu_fwd_workspace_size(-1, 128, 4, 4, 128, BF16) == 0
+    assert lib.hstu_fwd_workspace_size(2, 128, 4, 3, 128, BF16, 0) == 0
+    assert lib.hstu_fwd_workspace_size(-1, 128, 4, 4, 128, BF16, 0) == 0
+    # different Q/K lengths reserve the partial sums of key-split items
+    assert hj.hstu_fwd_workspace_size(32, 2048, 4, 4, 128, __import__("torch").bfloat16, is_delta_qk=True) > \
+        hj.hstu_fwd_workspace_size(32, 2048, 4, 4, 128, __import__("torch").bfloat16)
     assert lib.hstu_fwd_paged_workspace_size(64, 64, 4160, 4, 4, 128, BF16) > 0
 
 
