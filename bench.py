@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--all", action="store_true", help="one JSON line per workload (extra lines for analysis)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 1 GiB device copies (the reference point for the HBM byte counters)")
+    ap.add_argument("--traffic-record", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                          "COPY_WRITE_DIR"),
+                    help="CPU only: turn the four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of this "
+                         "workload and of --copy-calibration) into profiles/fwd_kernel_<WORKLOAD>_traffic.{json,txt}")
     return ap.parse_args()
 
 
@@ -73,6 +77,74 @@ def measured_traffic(name):
     return rec.get("traffic_bytes_per_launch")
 
 
+def _counter_rows(folder, counter):
+    """(kernel name, value) of every dispatch in the rocprofv3 counter CSVs under folder."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def traffic_record(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Writes the HBM traffic record of the forward kernel on one workload:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two separate
+    rocprofv3 --pmc runs of this script on the workload), each scaled by
+    what the same counter reads for the plain 1 GiB copies of
+    --copy-calibration, against the algorithmic bytes of one launch."""
+    import statistics
+    copy_kib = COPY_BYTES / 1024.0
+    cf = [v for k, v in _counter_rows(copy_fetch_dir, "FETCH_SIZE") if "copyBuffer" in k]
+    cw = [v for k, v in _counter_rows(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k]
+    fetch_factor = copy_kib / statistics.mean(cf)
+    write_factor = copy_kib / statistics.mean(cw)
+    fk = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if "fwd_kernel" in k]
+    wk = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if "fwd_kernel" in k]
+    fetch, write = statistics.mean(fk), statistics.mean(wk)
+    traffic = (fetch * fetch_factor + write * write_factor) * 1024.0
+    from hstu_jagged_attention_amd import workloads as wl
+    _, alg_bytes, _ = workload_work(name, wl.WORKLOADS[name]())
+    rec = {"workload": name, "kernel": "fwd_kernel", "kernel_source_sha256": kernel_source_sha256(),
+           "fetch_kib_per_dispatch": round(fetch, 3), "write_kib_per_dispatch": round(write, 3),
+           "fetch_factor": round(fetch_factor, 5), "write_factor": round(write_factor, 5),
+           "traffic_bytes_per_launch": int(round(traffic)), "algorithmic_bytes_per_launch": int(round(alg_bytes)),
+           "dispatches": len(fk)}
+    base = os.path.join(ROOT, "profiles", f"fwd_kernel_{name}_traffic")
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+    run = "python3 REPO/bench.py"
+    lines = [
+        f"fwd_kernel HBM traffic on workload {name} (rocprofv3 --pmc, one counter per run)", "",
+        "Commands (each run from /tmp with TMPDIR=/tmp; REPO = repository root):",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/prof/{name}_FETCH_SIZE -o p -- "
+        f"{run} --workload {name} --steps 10 --warmup 2 --no-cpu-baseline",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/prof/{name}_WRITE_SIZE -o p -- "
+        f"{run} --workload {name} --steps 10 --warmup 2 --no-cpu-baseline",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/prof/copy_FETCH_SIZE -o p -- "
+        f"{run} --copy-calibration",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/prof/copy_WRITE_SIZE -o p -- "
+        f"{run} --copy-calibration",
+        f"  {run} --traffic-record {name} <the four -d folders above>   (this summary)", "",
+        f"Copy calibration (__amd_rocclr_copyBuffer, 1 GiB read + 1 GiB written = {copy_kib:.0f} KiB each):",
+        f"  FETCH_SIZE reads {statistics.mean(cf):.1f} KiB -> fetch factor {fetch_factor:.5f}",
+        f"  WRITE_SIZE reads {statistics.mean(cw):.1f} KiB -> write factor {write_factor:.5f}", "",
+        f"fwd_kernel, per dispatch ({len(fk)} dispatches):",
+        f"  FETCH_SIZE mean {fetch:.1f} KiB (min {min(fk):.1f}, max {max(fk):.1f})",
+        f"  WRITE_SIZE mean {write:.1f} KiB (min {min(wk):.1f}, max {max(wk):.1f})",
+        f"  traffic = (FETCH*{fetch_factor:.4f} + WRITE*{write_factor:.4f}) KiB = {traffic / 1e6:.2f} MB per launch",
+        f"  algorithmic bytes per launch = {alg_bytes / 1e6:.2f} MB; traffic / algorithmic = {traffic / alg_bytes:.2f}",
+        f"kernel source sha256 {kernel_source_sha256()}", ""]
+    with open(base + ".txt", "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def copy_calibration(dev):
     """Plain device-to-device copies of COPY_BYTES each (read COPY_BYTES, write
     COPY_BYTES): the reference kernel for scaling the byte counters."""
@@ -86,36 +158,21 @@ def copy_calibration(dev):
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 5}), flush=True)
 
 
-def build_step(name, dev):
-    import torch
-    import hstu_jagged_attention_amd as hj
+def workload_work(name, c):
+    """Effective flops, algorithmic HBM bytes per launch and the config
+    description of a workload (host-side accounting, no GPU)."""
     from hstu_jagged_attention_amd import metrics
-    from hstu_jagged_attention_amd import workloads as wl
-    c = wl.WORKLOADS[name]()
+    E = ELEM[c.dtype]
     if name == "bf16_paged_target":
-        prep = hj.prepare_fwd_paged(c.q.to(dev), c.k_new.to(dev), c.v_new.to(dev), c.kv_cache.to(dev),
-                                    torch.as_tensor(c.seq_offsets_q), torch.as_tensor(c.page_offsets),
-                                    torch.as_tensor(c.page_ids), torch.as_tensor(c.last_page_len),
-                                    num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
-                                    mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                                    out_scale=c.out_scale)
         pairs = metrics.pairs_paged(c.history_lengths, c.new_lengths, c.num_context, c.num_targets,
                                     c.target_group_size, c.mask_type)
         Tq = int(c.seq_offsets_q[-1])
         alg_bytes = metrics.algorithmic_bytes_paged(Tq, int(c.history_lengths.sum()), c.num_heads_q, c.num_heads_kv,
-                                                    c.head_dim, ELEM[c.dtype])
+                                                    c.head_dim, E)
         desc = dict(batch=c.batch, history="U{512..4096}", new_tokens="U{1..64}", page_size=c.page_size,
                     total_new_tokens=Tq, total_history_tokens=int(c.history_lengths.sum()))
     else:
-        prep = hj.prepare_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets),
-                              rab=None if c.rab is None else c.rab.to(dev),
-                              mask=None if c.mask is None else c.mask.to(dev),
-                              seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
-                              num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
-                              mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                              out_scale=c.out_scale)
         T, Tk = int(c.seq_offsets[-1]), int(c.key_lengths.sum())
-        E = ELEM[c.dtype]
         if c.mask is not None:
             m = c.mask.float().numpy()
             total, rab_entries = metrics.user_mask_counts(m, c.lengths, c.num_heads_q,
@@ -142,8 +199,32 @@ def build_step(name, dev):
             desc.update(user_mask_heads=int(c.mask.shape[1]), rab_heads=0 if c.rab is None else int(c.rab.shape[1]))
     flops = metrics.effective_flops(pairs, c.num_heads_q, c.head_dim)
     desc.update(num_heads_q=c.num_heads_q, num_heads_kv=c.num_heads_kv, head_dim=c.head_dim,
-                mask={0: "causal", 2: "bidirectional", 3: "user mask"}[c.mask_type], rab=bool(getattr(c, "rab", None) is not None),
-                visible_pairs_per_head=pairs)
+                mask={0: "causal", 2: "bidirectional", 3: "user mask"}[c.mask_type],
+                rab=bool(getattr(c, "rab", None) is not None), visible_pairs_per_head=pairs)
+    return flops, alg_bytes, desc
+
+
+def build_step(name, dev):
+    import torch
+    import hstu_jagged_attention_amd as hj
+    from hstu_jagged_attention_amd import workloads as wl
+    c = wl.WORKLOADS[name]()
+    if name == "bf16_paged_target":
+        prep = hj.prepare_fwd_paged(c.q.to(dev), c.k_new.to(dev), c.v_new.to(dev), c.kv_cache.to(dev),
+                                    torch.as_tensor(c.seq_offsets_q), torch.as_tensor(c.page_offsets),
+                                    torch.as_tensor(c.page_ids), torch.as_tensor(c.last_page_len),
+                                    num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                                    mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                                    out_scale=c.out_scale)
+    else:
+        prep = hj.prepare_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets),
+                              rab=None if c.rab is None else c.rab.to(dev),
+                              mask=None if c.mask is None else c.mask.to(dev),
+                              seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
+                              num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                              mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                              out_scale=c.out_scale)
+    flops, alg_bytes, desc = workload_work(name, c)
     return c, prep, flops, alg_bytes, desc
 
 
@@ -259,6 +340,9 @@ def measure(name, args, dev):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
               "path; see the sharding note in the design document)", file=sys.stderr)
