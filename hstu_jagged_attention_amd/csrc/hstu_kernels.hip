@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // independent chains, and every result is used EB instructions after
       // it is made.
       auto epi_block = [&](auto masked, int jb) {
-        constexpr int EB = (RAB || MSK) ? 8 : 16;  // elements per pass (rab / mask values hold registers too)
+        constexpr int EB = (RAB || MSK) ? 4 : 16;  // elements per pass (rab / mask values hold registers too)
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += EB) {
           float y[EB], e[EB];
