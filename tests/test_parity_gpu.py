@@ -347,3 +347,45 @@ def test_next_workloads_full_size_sampled(dev, name):
     ref = oracle_jagged_sampled(c, _picks(c))
     for b, (toks, heads, vals) in ref.items():
         assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, c.dtype, f"{name} seq {b}")
+
+
+# ------------------------------------------------------------ HIP graph capture
+def _prepare(c, dev):
+    return hj.prepare_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets),
+                          rab=None if c.rab is None else c.rab.to(dev),
+                          seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
+                          num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                          mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                          out_scale=c.out_scale)
+
+
+@pytest.mark.parametrize("name,batch", [("bf16_mha_causal", 8), ("fp16_gqa_causal", 2), ("bf16_delta_qk", 6)])
+def test_plan_and_run_replay_in_a_hip_graph(dev, name, batch):
+    """plan + run captured in one HIP graph (direct mode, the work list with
+    its queue counters, and key-split items with the ordered reduction):
+    every replay, with eager launches of another call in between, equals the
+    eager result bit for bit, so the counters the run rewinds and the plan
+    rewrites survive replays."""
+    c = wl.WORKLOADS[name](batch=batch)
+    say("graph", name, "batch", batch)
+    other = wl.bf16_mha_causal(batch=2)
+    s = torch.cuda.Stream(dev)
+    with torch.cuda.stream(s):
+        prep = _prepare(c, dev)
+        prep_other = _prepare(other, dev)
+        prep.plan()
+        prep.run()
+        s.synchronize()
+        eager = prep.out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            prep.plan()
+            prep.run()
+        for _ in range(4):
+            prep.out.zero_()
+            g.replay()
+            s.synchronize()
+            assert torch.equal(prep.out, eager)
+            prep_other.fwd()  # eager work on the same stream between replays
+            s.synchronize()
+    assert_parity(eager, oracle_jagged(c), c.dtype, f"graph {name}")
