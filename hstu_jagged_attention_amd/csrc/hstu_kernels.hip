@@ -3,31 +3,38 @@
 // Operation (RecOps Running Case Documentation, HSTU_V1 forward operator:
 // feature table, operator introduction, inputs/outputs table): per query
 // head, O = out_scale * (M .* silu(alpha * (Q K^T + rab))) V over jagged
-// sequences, MHA or GQA, with the bidirectional mask or the causal mask
-// built from num_context / num_targets / target_group_size, and a paged
-// variant whose history K/V live in kv_cache pages. No softmax: partial sums
-// over key tiles add exactly, so no running max or rescale is kept.
+// sequences, MHA or GQA, with the bidirectional mask, the causal mask built
+// from num_context / num_targets / target_group_size, or the user's mask
+// tensor (mask_type 3, whose values multiply P); rab may be shared by all
+// heads ([B, 1, S, S]); queries may be the last positions of longer key
+// sequences (seq_offsets_k); and a paged variant reads history K/V from
+// kv_cache pages. No softmax: partial sums over key tiles add exactly, so no
+// running max or rescale is kept.
 //
 // Kernels per call, all on the caller's stream:
 //  1. plan_kernel: one workgroup turns seq_offsets (and the mask inputs)
 //     into the work list: one item per (sequence, query tile), costed by the
 //     number of key tiles that are not fully masked, counting-sorted longest
-//     first. It also zeroes the work-queue counter.
-//  2. fwd_kernel: persistent workgroups of 4 waves pop items from the queue
-//     in list order. A workgroup owns one item and a group of query heads
-//     that share one kv head (1 head x 128 rows for MHA, up to 4 heads x 32
-//     rows for GQA), so each K/V tile is staged through LDS once for all of
-//     them. K/V tiles go global -> LDS by DMA (no register staging), double
-//     buffered, rows stored as 16-byte chunks under an XOR swizzle. Per key
-//     tile: S^T = K Q^T on MFMA (the accumulator then holds one query per
-//     lane and 16 keys per lane), the SiLU epilogue in registers, then
-//     O^T += V^T P^T on MFMA with P used straight from the S^T registers as
-//     the B operand; the V^T A operand comes from transposing LDS reads of
-//     the row-major V tile, taken in the key order the S^T accumulator
-//     holds (bits 2 and 3 of the key index inside a 32-key block swapped).
-//  3. reduce_kernel (paged calls with split items only): items longer than
-//     the planner's chunk size run as several key-range chunks that store
-//     fp32 partial O; this kernel sums them in chunk order.
+//     first. It also zeroes the work-queue counter. Small batches skip it
+//     (direct mode: workgroup w runs item w of the full grid).
+//  2. fwd_kernel: persistent workgroups of 4 waves (8 in the key-split
+//     variant) pop items from the queue in list order. A workgroup owns one
+//     item and a group of query heads that share one kv head (1 head x 128
+//     rows for MHA, up to 4 heads x 32 rows for GQA), so each K/V tile is
+//     staged through LDS once for all of them. K/V tiles go global -> LDS by
+//     DMA (no register staging), double buffered, into rows padded so every
+//     fragment read is conflict-free. Per key tile: S^T = K Q^T on MFMA (the
+//     accumulator then holds one query per lane and 16 keys per lane), the
+//     SiLU epilogue in registers, then O^T += V^T P^T on MFMA with P used
+//     straight from the S^T registers as the B operand; the V^T A operand
+//     comes from transposing LDS reads of the row-major V tile, taken in the
+//     key order the S^T accumulator holds.
+//  3. reduce_kernel (calls with split items only: paged, and jagged with
+//     separate key offsets): items longer than the planner's chunk size run
+//     as several key-range chunks that store fp32 partial O; this kernel
+//     sums them in chunk order.
+//  fwd_kernel_f32 is the fp32 path (v_mfma_f32_32x32x2f32, K/V staged
+//  through registers).
 //
 // MFMA lane layouts (checked on the device): v_mfma_f32_32x32x16_{bf16,f16}
 // takes A[m = lane%32][k = 8*(lane/32) + 0..7] and B[k = 8*(lane/32) + 0..7]
