@@ -1413,13 +1413,13 @@ KernelFn pick16(bool causal, bool rab, bool ksplit, bool user_mask) {
   constexpr int WPE = D >= 256 ? 1 : 2;
   if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE, 1> : fwd_kernel<T, D, BN, false, false, true, WPE, 1>;
   if (user_mask) {
-    // The user-mask kernels hold a second prefetched tile (the mask values)
-    // and run out of registers at two waves per SIMD from head_dim 128; one
-    // wave per SIMD (512 registers, the in-wave pipelined body) measured 22 %
-    // faster there. The built-in-mask kernels measured slower that way.
-    constexpr int WPE_M = D >= 128 ? 1 : WPE;
-    return rab ? fwd_kernel<T, D, BN, false, true, false, WPE_M, 1, true>
-               : fwd_kernel<T, D, BN, false, false, false, WPE_M, 1, true>;
+    // The user-mask kernels hold a second prefetched tile (the mask values).
+    // At head_dim 128 they take 32-key tiles, which halves the prefetched
+    // and S^T / P registers: measured 86 -> 67 us on the user-mask workload
+    // (64-key tiles spilled at two waves per SIMD and ran best at one).
+    constexpr int BNM = D == 128 ? 32 : BN;
+    return rab ? fwd_kernel<T, D, BNM, false, true, false, WPE, 1, true>
+               : fwd_kernel<T, D, BNM, false, false, false, WPE, 1, true>;
   }
   if constexpr (BN == 64) {
     if (ksplit) {
@@ -1451,7 +1451,7 @@ template <bool PAGED>
 KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, bool user_mask, int* wgs_per_cu, int* threads) {
   ksplit = ksplit && !PAGED && dt != DType::F32 && D <= 128 && !user_mask;
   if (user_mask && (PAGED || dt == DType::F32)) return nullptr;
-  *wgs_per_cu = ksplit ? 1 : ((dt == DType::F32 || D >= 256 || (user_mask && D >= 128)) ? 1 : 2);
+  *wgs_per_cu = ksplit ? 1 : ((dt == DType::F32 || D >= 256) ? 1 : 2);
   *threads = ksplit ? 2 * kThreads : kThreads;
   switch (dt) {
     case DType::BF16:
@@ -1602,7 +1602,7 @@ KParams make_params(const FwdArgs& a) {
   // multiplies by y = c s (Q pre-scaled) and folds -1/log2(e) instead.
   p.c_exp = -a.alpha * kLog2e;
   p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : -a.out_scale / kLog2e;
-  const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256 || (a.user_mask && a.head_dim >= 128);
+  const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256;
   p.target_chunks = num_cus() * (one_wave ? 1 : 2);
   return p;
 }
