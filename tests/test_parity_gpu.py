@@ -389,3 +389,42 @@ def test_plan_and_run_replay_in_a_hip_graph(dev, name, batch):
             prep_other.fwd()  # eager work on the same stream between replays
             s.synchronize()
     assert_parity(eager, oracle_jagged(c), c.dtype, f"graph {name}")
+
+
+# ------------------------------------------------------------ seeded random configurations
+def _random_case(i):
+    """Configuration i of a seeded sweep over the ABI's space: dtype, head
+    dim, head counts, ragged and empty lengths, the three mask kinds with
+    context / targets / groups, rab with one or all heads, odd max_seq_len,
+    and different Q/K lengths."""
+    rng = np.random.default_rng(9000 + i)
+    dt = ["bf16", "f16", "f32"][i % 3]
+    D = int(rng.choice([32, 64, 128] if dt == "f32" else [32, 64, 128, 256]))
+    Hq, Hk = [(1, 1), (2, 1), (4, 4), (4, 2), (6, 3), (8, 2)][int(rng.integers(6))]
+    B = int(rng.integers(1, 6))
+    lk = rng.integers(0, 300, size=B)
+    lk[int(rng.integers(B))] = max(int(lk.max()), 1)
+    mask = int(rng.choice([CAUSAL, NONE, CUSTOM] if dt != "f32" else [CAUSAL, NONE]))
+    delta = bool(rng.integers(2))
+    lq = np.minimum(rng.integers(1, 80, size=B), lk) if delta else None
+    S = int(lk.max()) + int(rng.integers(0, 3))
+    kw = {}
+    if mask == CAUSAL:
+        kw.update(num_context=(0, 40) if rng.integers(2) else None,
+                  num_targets=(0, 60) if rng.integers(2) else None, target_group_size=int(rng.integers(0, 4)))
+    if rng.integers(2):
+        kw.update(rab_std=0.2, rab_heads=int(rng.choice([1, Hq])))
+    if mask == CUSTOM:
+        kw.update(mask_keep=float(rng.uniform(0.2, 0.9)), mask_heads=int(rng.choice([1, Hq])))
+    return wl.jagged_case(9000 + i, lk, Hq, Hk, D, dt, mask_type=mask, max_seq_len=S, q_lengths=lq,
+                          name=f"random_{i}", **kw)
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_configurations(dev, i):
+    c = _random_case(i)
+    say(c.name, c.dtype, "D", c.head_dim, "heads", c.num_heads_q, c.num_heads_kv, "mask", c.mask_type,
+        "keys", c.key_lengths.tolist(), "queries", c.lengths.tolist(), "rab", c.rab is not None,
+        "S", c.max_seq_len)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), c.dtype, c.name)
