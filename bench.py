@@ -121,14 +121,14 @@ def traffic_record(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     run = "python3 REPO/bench.py"
     lines = [
         f"fwd_kernel HBM traffic on workload {name} (rocprofv3 --pmc, one counter per run)", "",
-        "Commands (each run from /tmp with TMPDIR=/tmp; REPO = repository root):",
-        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/prof/{name}_FETCH_SIZE -o p -- "
+        "Commands (each run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = any output folder):",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/{name}_FETCH_SIZE -o p -- "
         f"{run} --workload {name} --steps 10 --warmup 2 --no-cpu-baseline",
-        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/prof/{name}_WRITE_SIZE -o p -- "
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/{name}_WRITE_SIZE -o p -- "
         f"{run} --workload {name} --steps 10 --warmup 2 --no-cpu-baseline",
-        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/prof/copy_FETCH_SIZE -o p -- "
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_FETCH_SIZE -o p -- "
         f"{run} --copy-calibration",
-        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/prof/copy_WRITE_SIZE -o p -- "
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_WRITE_SIZE -o p -- "
         f"{run} --copy-calibration",
         f"  {run} --traffic-record {name} <the four -d folders above>   (this summary)", "",
         f"Copy calibration (__amd_rocclr_copyBuffer, 1 GiB read + 1 GiB written = {copy_kib:.0f} KiB each):",
@@ -344,7 +344,7 @@ def main():
         traffic_record(*args.traffic_record)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no multi-GPU "
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library has no multi-GPU "
               "path; see the sharding note in the design document)", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -276,7 +276,7 @@ const char* hstu_status_string(hstu_status_t status) {
     case HSTU_ERR_INVALID_ARG:
       return "HSTU_ERR_INVALID_ARG: invalid argument";
     case HSTU_ERR_UNSUPPORTED:
-      return "HSTU_ERR_UNSUPPORTED: valid but not supported by this build";
+      return "HSTU_ERR_UNSUPPORTED: valid but not supported by this library";
     case HSTU_ERR_WORKSPACE:
       return "HSTU_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case HSTU_ERR_HIP:
