@@ -87,7 +87,7 @@ struct KParams {
   int32_t* split_items;  // split items: two ints each (see the planner)
   int32_t* n_split;      // number of split items
   int32_t split_slots;   // partial-sum slots available (0: never split)
-  int32_t target_chunks; // chunks the planner aims for (about 2 per resident workgroup)
+  int32_t target_chunks; // chunks the planner aims for (one per two resident workgroups)
   int32_t* counter;   // work-queue head
   int32_t* exited;    // workgroups that left the queue (the last one resets both counters)
   int32_t batch;
@@ -196,8 +196,9 @@ __device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, bool
 // n_chunks partial-sum slots of a split item (0xffff when not split).
 // Split items are also listed once each in the reduction list:
 // (b << 16) | q_tile, (n_chunks << 16) | slot.
-// Chunk size: the average work per resident workgroup (at least
-// kMinChunkTiles), doubled until the split items fit the partial-sum slots.
+// Chunk size: the total work over target_chunks (one chunk per two resident
+// workgroups; at least kMinChunkTiles), doubled until the split items fit
+// the partial-sum slots.
 // ------------------------------------------------------------------------
 // Wave-wide inclusive prefix sum (64 lanes) by DPP lane shifts: within each
 // row of 16 lanes by shifts of 1, 2, 4 and 8, then across rows by the
@@ -1611,7 +1612,10 @@ KParams make_params(const FwdArgs& a) {
   p.c_exp = -a.alpha * kLog2e;
   p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : -a.out_scale / kLog2e;
   const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256;
-  p.target_chunks = num_cus() * (one_wave ? 1 : 2);
+  // One chunk per two resident workgroups: measured against 4x, 2x, 1/2x and
+  // 1/4x that on the paged and delta-QK workloads (fewer chunks lengthen the
+  // critical path; more of them cost partial-sum traffic and reduction time).
+  p.target_chunks = num_cus() * (one_wave ? 1 : 2) / 2;
   return p;
 }
 
