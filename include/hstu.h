@@ -60,7 +60,8 @@ extern "C" {
 typedef enum {
   HSTU_OK = 0,
   HSTU_ERR_INVALID_ARG = 1, /* bad size, null required pointer, misaligned pointer, bad combination */
-  HSTU_ERR_UNSUPPORTED = 2, /* valid per the page but not built here (mask codes 1/3, head_dim, page_size) */
+  HSTU_ERR_UNSUPPORTED = 2, /* valid per the page but not built here (mask code 1, the user mask in f32 or
+                               paged, head_dim, page_size) */
   HSTU_ERR_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
   HSTU_ERR_HIP = 4          /* a HIP launch failed; the HIP error is left for hipGetLastError */
 } hstu_status_t;
@@ -72,7 +73,9 @@ typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2, HSTU_MASK_CUSTOM = 3 } 
 /* Supported sizes: head_dim in {32, 64, 128, 256} for f16/bf16 and
  * {32, 64, 128} for f32 (the page allows multiples of 16 up to 512);
  * num_heads_q % num_heads_kv == 0 (the page's GQA rule); page_size in
- * {32, 64, 128, 256}; max_seq_len in [1, 20480]. */
+ * {32, 64, 128, 256}; max_seq_len in [1, 20480]; rab and user-mask head
+ * counts 1 or num_heads_q; the user mask (HSTU_MASK_CUSTOM) in f16/bf16
+ * jagged calls. */
 
 /*
  * Workspace bytes hstu_fwd needs for these sizes (the work list of the tile
