@@ -5,13 +5,20 @@ One step = the whole hot path over one batch of synthetic input already
 resident in HBM: the tile scheduler (hstu_*_plan) and the fused forward
 kernel (hstu_*_run), both through the C ABI. Prints ONE JSON line:
 effective TFLOP/s = 4 * head_dim * (visible query/key pairs summed over
-query heads) / wall time per step, with the dominant kernel's roofline
-(achieved vs MI355X's dense MFMA peak, per-launch time from HIP events on
-the launch stream) and the float64 CPU oracle timed on the host as a
-baseline.
+query heads) / time per step, with the dominant kernel's roofline (achieved
+vs MI355X's dense MFMA peak, or vs HBM bandwidth for the workloads that
+stream rab, a user mask or a KV cache) and the float64 CPU oracle timed on
+the host as a baseline.
 
-Default workload: bf16 MHA jagged causal, batch 8, lengths ~ U{256..1024},
-4 heads, head_dim 128.
+Timing is cold by default: before every timed step a 1 GiB device buffer is
+written (outside the timed events), which evicts the inputs from the L2
+caches and the 256 MB Infinity Cache, so every step reads them from HBM.
+Steps are timed with HIP events on the launch stream. Back-to-back (warm)
+steps are reported as secondary keys.
+
+Default workload: fp16 GQA jagged causal, batch 16, lengths lognormal
+(median 1500, clipped to [128, 4096]), 8 query heads sharing 2 kv heads,
+head_dim 128 -- the largest configuration that fits one GPU.
 """
 from __future__ import annotations
 
@@ -28,18 +35,30 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
 ELEM = {"bf16": 2, "f16": 2, "f32": 4}
+FLUSH_BYTES = 1 << 30  # written before each cold step: > 256 MB Infinity Cache + 8 x 4 MB L2
+
+# The roof that binds each workload's forward kernel (algorithmic flops and
+# bytes per launch at MI355X's dense MFMA and HBM peaks): MFMA for the
+# causal and GQA workloads, HBM for the ones that stream rab, a user mask
+# or a KV cache. The tiny fp32 workload is launch-bound; its line is
+# priced against the fp32 MFMA peak.
+BOUND = {"tiny_fp32_bidirectional": "mfma", "bf16_mha_causal": "mfma", "fp16_gqa_causal": "mfma",
+         "bf16_rab_target": "hbm", "bf16_paged_target": "hbm", "bf16_custom_mask": "hbm", "bf16_delta_qk": "hbm"}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="bf16_mha_causal")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp16_gqa_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload (extra lines for analysis)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only plain 1 GiB device copies (the reference point for the HBM byte counters)")
+    ap.add_argument("--counter-summary", nargs="+", metavar=("WORKLOAD", "DIR"),
+                    help="CPU only: turn rocprofv3 --pmc output folders (the passes of COUNTER_PASSES) into "
+                         "profiles/counters_<WORKLOAD>.txt")
     ap.add_argument("--traffic-record", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR"),
                     help="CPU only: turn the four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of this "
@@ -145,6 +164,79 @@ def traffic_record(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print("\n".join(lines))
 
 
+# Counter passes of --counter-summary, each within one run's hardware limits
+# (at most 8 SQ, 4 TCC and 2 GRBM counters; derived counters count their
+# inputs).
+COUNTER_PASSES = {
+    "util": "MfmaUtil VALUBusy SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16",
+    "insts": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_SALU "
+             "SQ_WAIT_INST_LDS SQ_WAVE_CYCLES",
+    "l2": "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+}
+
+
+def counter_summary(name, folders):
+    """Writes profiles/counters_<name>.txt from rocprofv3 --pmc CSV folders
+    (one folder per pass of COUNTER_PASSES, each a run of this script on the
+    workload): per-dispatch means of every counter over the forward kernel's
+    dispatches, and the ratios read from them."""
+    import csv
+    import glob
+    import statistics
+    from hstu_jagged_attention_amd import workloads as wl
+    vals, kernels = {}, set()
+    for folder in folders:
+        for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if "fwd_kernel" not in r["Kernel_Name"]:
+                        continue
+                    kernels.add(r["Kernel_Name"].split("(")[0][:120])
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no fwd_kernel counter rows under {folders}")
+    m = {k: statistics.mean(v) for k, v in vals.items()}
+    flops, alg_bytes, _ = workload_work(name, wl.WORKLOADS[name]())
+    lines = [f"fwd_kernel hardware counters on workload {name} (rocprofv3 --pmc, per-dispatch means)", "",
+             "Commands (each run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = any output folder):"]
+    for pas, ctrs in COUNTER_PASSES.items():
+        lines.append(f"  timeout -s KILL 120 rocprofv3 --pmc {ctrs} --output-format csv -d OUT/{name}_{pas} -o p -- "
+                     f"python3 REPO/bench.py --workload {name} --steps 3 --warmup 1 --no-cpu-baseline")
+    lines.append(f"  python3 REPO/bench.py --counter-summary {name} " +
+                 " ".join(f"OUT/{name}_{p}" for p in COUNTER_PASSES) + "   (this summary)")
+    lines += ["", "Kernel: " + ", ".join(sorted(kernels)), "", "Counters (mean per dispatch):"]
+    for k in sorted(m):
+        lines.append(f"  {k:32s} {m[k]:16.1f}   ({len(vals[k])} dispatches)")
+    lines += ["", "Read from them:"]
+    mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+    if "MfmaUtil" in m:
+        lines.append(f"  MFMA busy (MfmaUtil)                      {m['MfmaUtil']:.1f} % of SIMD-cycles")
+    if "VALUBusy" in m:
+        lines.append(f"  VALU busy (VALUBusy)                      {m['VALUBusy']:.1f} %")
+    if mops:
+        lines.append(f"  MFMA flops executed / effective           {mops * 512 / flops:.3f}  "
+                     f"(executed {mops * 512 / 1e9:.2f} GFLOP, effective {flops / 1e9:.2f} GFLOP)")
+    if m.get("SQ_INSTS_MFMA"):
+        mf = m["SQ_INSTS_MFMA"]
+        lines.append(f"  VALU instructions per MFMA                {m.get('SQ_INSTS_VALU', 0.0) / mf:.2f}  "
+                     "(SQ_INSTS_VALU counts the MFMAs too)")
+        lines.append(f"  fp32 transcendentals per MFMA             {m.get('SQ_INSTS_VALU_TRANS_F32', 0.0) / mf:.2f}")
+        lines.append(f"  LDS instructions per MFMA                 {m.get('SQ_INSTS_LDS', 0.0) / mf:.2f}")
+        lines.append(f"  SALU instructions per MFMA                {m.get('SQ_INSTS_SALU', 0.0) / mf:.2f}")
+    if m.get("SQ_INSTS_LDS"):
+        lines.append(f"  LDS bank-conflict cycles per LDS instr.   {m.get('SQ_LDS_BANK_CONFLICT', 0.0) / m['SQ_INSTS_LDS']:.3f}")
+    if m.get("SQ_WAVE_CYCLES"):
+        lines.append(f"  LDS-issue wait / wave cycles              {m.get('SQ_WAIT_INST_LDS', 0.0) / m['SQ_WAVE_CYCLES']:.3f}")
+    if "TCC_HIT_sum" in m:
+        hm = m["TCC_HIT_sum"] + m.get("TCC_MISS_sum", 0.0)
+        lines.append(f"  L2 (TCC) hit rate                         {m['TCC_HIT_sum'] / hm:.3f}  ({hm:.0f} requests)")
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", f"counters_{name}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def copy_calibration(dev):
     """Plain device-to-device copies of COPY_BYTES each (read COPY_BYTES, write
     COPY_BYTES): the reference kernel for scaling the byte counters."""
@@ -228,9 +320,22 @@ def build_step(name, dev):
     return c, prep, flops, alg_bytes, desc
 
 
-def cpu_baseline(c, name, flops_full):
-    """The float64 oracle on the host cores over the same inputs (whole
-    workload when that is a few seconds of CPU work, else a row sample)."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_sample(c, name, flops_full, stride):
+    """(run, flops, description) of one oracle pass over the workload: the
+    whole of it (stride 1) or every stride-th query row of every sequence,
+    all heads."""
     import numpy as np
     import oracle
     from hstu_jagged_attention_amd import metrics
@@ -239,99 +344,203 @@ def cpu_baseline(c, name, flops_full):
         return t.double().numpy()
 
     if name == "bf16_paged_target":
-        run = lambda: oracle.hstu_fwd_paged(f64(c.q), f64(c.k_new), f64(c.v_new), f64(c.kv_cache), c.seq_offsets_q,
-                                            c.page_offsets, c.page_ids, c.last_page_len, num_context=c.num_context,
-                                            num_targets=c.num_targets, mask_type=c.mask_type,
-                                            target_group_size=c.target_group_size, alpha=c.alpha,
-                                            out_scale=c.out_scale)
-        sample, fl = "whole workload", flops_full
-    elif name in ("bf16_mha_causal", "tiny_fp32_bidirectional", "bf16_custom_mask", "bf16_delta_qk"):
-        q, k, v = f64(c.q), f64(c.k), f64(c.v)
-        rab = None if c.rab is None else f64(c.rab)
-        mask = None if c.mask is None else f64(c.mask)
-        run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, mask=mask, seq_offsets_k=c.seq_offsets_k,
-                                      num_context=c.num_context, num_targets=c.num_targets,
-                                      max_seq_len=c.max_seq_len, mask_type=c.mask_type,
-                                      target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
-        sample, fl = "whole workload", flops_full
+        q, kn, vn, kv = f64(c.q), f64(c.k_new), f64(c.v_new), f64(c.kv_cache)
+        if stride == 1:
+            rows, fl, desc = None, flops_full, "whole workload"
+        else:
+            rows, pairs = [], 0
+            for b in range(c.batch):
+                q0, q1 = int(c.seq_offsets_q[b]), int(c.seq_offsets_q[b + 1])
+                Lh = int(c.history_lengths[b])
+                nc = 0 if c.num_context is None else int(c.num_context[b])
+                nt = 0 if c.num_targets is None else int(c.num_targets[b])
+                per_row = metrics.visible_per_row(Lh + q1 - q0, nc, nt, c.target_group_size, c.mask_type)
+                for t in range(q0, q1, stride):
+                    rows += [(t, h) for h in range(c.num_heads_q)]
+                    pairs += int(per_row[Lh + t - q0]) * c.num_heads_q
+            fl, desc = 4.0 * c.head_dim * pairs, f"every {stride}th new token of every request, all heads"
+        run = lambda: oracle.hstu_fwd_paged(q, kn, vn, kv, c.seq_offsets_q, c.page_offsets, c.page_ids,
+                                            c.last_page_len, num_context=c.num_context, num_targets=c.num_targets,
+                                            mask_type=c.mask_type, target_group_size=c.target_group_size,
+                                            alpha=c.alpha, out_scale=c.out_scale, rows=rows)
+        return run, fl, desc
+    q, k, v = f64(c.q), f64(c.k), f64(c.v)
+    rab = None if c.rab is None else f64(c.rab)
+    mask = None if c.mask is None else f64(c.mask)
+    if stride == 1:
+        rows, fl, desc = None, flops_full, "whole workload"
     else:
-        # Row sample: every 16th token of every sequence, all heads.
-        q, k, v = f64(c.q), f64(c.k), f64(c.v)
-        rows, pairs = [], 0
+        rows, frac = [], 0.0
         for b in range(c.batch):
             s0, L = int(c.seq_offsets[b]), int(c.lengths[b])
-            nc = 0 if c.num_context is None else int(c.num_context[b])
-            nt = 0 if c.num_targets is None else int(c.num_targets[b])
-            per_row = metrics.visible_per_row(L, nc, nt, c.target_group_size, c.mask_type)
-            for i in range(0, L, 16):
+            for i in range(0, L, stride):
                 rows += [(s0 + i, h) for h in range(c.num_heads_q)]
-                pairs += int(per_row[i]) * c.num_heads_q
-        rab = None if c.rab is None else f64(c.rab)
-        run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, num_context=c.num_context,
-                                      num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
-                                      target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale,
-                                      rows=rows)
-        sample, fl = "every 16th query row of every sequence, all heads", 4.0 * c.head_dim * pairs
-    # Repeat the sample until about 10 s of CPU work has been timed.
+        # Flops of the sample: the visible pairs of the sampled rows (query i
+        # of a sequence sits at key position Lk - Lq + i).
+        pairs = 0
+        m = None if c.mask is None else c.mask.float().numpy()
+        for b in range(c.batch):
+            Lq, Lk = int(c.lengths[b]), int(c.key_lengths[b])
+            pos = np.arange(0, Lq, stride) + (Lk - Lq)
+            if m is not None:
+                blk = np.nan_to_num(m[b, :, pos, :Lk], nan=0.0)
+                pairs += int(np.count_nonzero(blk)) * (c.num_heads_q // m.shape[1])
+            else:
+                nc = 0 if c.num_context is None else int(c.num_context[b])
+                nt = 0 if c.num_targets is None else int(c.num_targets[b])
+                per_row = metrics.visible_per_row(Lk, nc, nt, c.target_group_size, c.mask_type)
+                pairs += int(per_row[pos].sum()) * c.num_heads_q
+        fl = 4.0 * c.head_dim * pairs
+        desc = f"every {stride}th query row of every sequence, all heads"
+    run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, mask=mask, seq_offsets_k=c.seq_offsets_k,
+                                  num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+                                  mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
+                                  out_scale=c.out_scale, rows=rows)
+    return run, fl, desc
+
+
+def _time_for(run, seconds):
     runs, total = 0, 0.0
-    while runs == 0 or total < 10.0:
+    while runs == 0 or total < seconds:
         t0 = time.perf_counter()
         run()
         total += time.perf_counter() - t0
         runs += 1
-    return {"value": fl * runs / total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{sample}; {runs} runs in {total:.2f} s"}
+    return runs, total
+
+
+# Row strides of the oracle samples: (all host threads, one thread). The
+# whole small workloads take well under a second per pass; the large ones
+# are sampled so that each figure takes about 10 s (all threads) and 5 s
+# (one thread) of CPU time.
+ORACLE_STRIDES = {"tiny_fp32_bidirectional": (1, 1), "bf16_mha_causal": (1, 8), "bf16_rab_target": (16, 128),
+                  "fp16_gqa_causal": (16, 128), "bf16_paged_target": (1, 8), "bf16_custom_mask": (1, 8),
+                  "bf16_delta_qk": (1, 8)}
+
+
+def cpu_baseline(c, name, flops_full):
+    """The float64 oracle (as it stands) on the host's cores over the same
+    inputs, then on one thread over a smaller sample."""
+    import oracle
+    s_all, s_one = ORACLE_STRIDES[name]
+    threads = oracle.num_threads()
+    run, fl, desc = oracle_sample(c, name, flops_full, s_all)
+    runs, total = _time_for(run, 10.0)
+    res = {"value": fl * runs / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{desc}; {runs} runs in {total:.2f} s on {threads} threads", "cpu_model": cpu_model()}
+    run1, fl1, desc1 = oracle_sample(c, name, flops_full, s_one)
+    oracle.set_num_threads(1)
+    try:
+        runs1, total1 = _time_for(run1, 5.0)
+    finally:
+        oracle.set_num_threads(threads)
+    res["single_thread"] = {"value": fl1 * runs1 / total1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                            "sample": f"{desc1}; {runs1} runs in {total1:.2f} s"}
+    return res
+
+
+def split_keys(c):
+    """True when the library splits long items over the key range (paged
+    calls and jagged calls with their own key offsets, 16-bit dtypes): the
+    run phase then also launches the ordered reduction kernel."""
+    return c.dtype != "f32" and (hasattr(c, "kv_cache") or getattr(c, "seq_offsets_k", None) is not None)
 
 
 def measure(name, args, dev):
+    import statistics
     import torch
     c, prep, flops, alg_bytes, desc = build_step(name, dev)
     stream = torch.cuda.current_stream(dev)
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    fill = [0]
+
+    def flush():
+        # A write of the whole buffer (a fresh value each time) evicts the
+        # inputs from every L2 and from the Infinity Cache.
+        fill[0] += 1
+        flush_buf.fill_(fill[0])
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
     for _ in range(args.warmup):
+        flush()
         prep.plan()
         prep.run()
     torch.cuda.synchronize(dev)
-    # Timed region: exactly K steps.
+
+    # Timed region: exactly K cold steps. Each step is bracketed by HIP
+    # events on the launch stream; the cache flush before it is not.
+    marks = [(ev(), ev()) for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e0, e1 in marks:
+        flush()
+        e0.record(stream)
         prep.plan()
         prep.run()
+        e1.record(stream)
     torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    # Per-kernel launch durations with HIP events on the launch stream: K
-    # back-to-back launches of one phase between two events, so the event
-    # markers' own latency is amortised over K launches (a plan stays valid
-    # for any number of runs: the run kernel rewinds its queue counters).
-    def timed(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    region_wall_ms = (time.perf_counter() - t0) * 1e3
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in marks]
+    ms_per_step = statistics.mean(step_ms)
+
+    # The run phase alone (the forward kernel, plus the ordered reduction of
+    # split items), cold: plan, flush, then events around the run.
+    rmarks = [(ev(), ev()) for _ in range(args.steps)]
+    for e0, e1 in rmarks:
+        prep.plan()
+        flush()
         e0.record(stream)
-        for _ in range(n):
+        prep.run()
+        e1.record(stream)
+    torch.cuda.synchronize(dev)
+    run_ms = statistics.mean(e0.elapsed_time(e1) for e0, e1 in rmarks)
+
+    # Warm (secondary): K back-to-back steps, then K back-to-back runs and
+    # plans, each group between two events (their latency amortised over K).
+    def warm(fn):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(args.steps):
             fn()
         e1.record(stream)
         torch.cuda.synchronize(dev)
-        return e0.elapsed_time(e1) / n
+        return e0.elapsed_time(e1) / args.steps
 
-    n_ev = max(args.steps, 10)
-    plan_ms = timed(prep.plan, n_ev)
+    warm_step_ms = warm(lambda: (prep.plan(), prep.run()))
     prep.plan()
-    run_ms = timed(prep.run, n_ev)
-    achieved_tflops = flops / (run_ms * 1e-3) / 1e12
+    warm_run_ms = warm(prep.run)
+    plan_ms = warm(prep.plan)
+
     dtype = c.dtype
-    peak = PEAK_TFLOPS[dtype]
+    peak_f = PEAK_TFLOPS[dtype]
+    mfma_tflops = flops / (run_ms * 1e-3) / 1e12
     hbm_gbs = alg_bytes / (run_ms * 1e-3) / 1e9
-    roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved_tflops / peak, 4), "traffic": measured_traffic(name),
-                "kernel": "fwd_kernel" + ("+reduce_kernel" if name == "bf16_paged_target" else ""),
-                "launch_ms_mean": round(run_ms, 5),
-                "plan_kernel_ms_mean": round(plan_ms, 5), "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
-                "algorithmic_hbm_GBps": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
+    bound = BOUND[name]
+    if bound == "mfma":
+        achieved, peak, unit = mfma_tflops, peak_f, "TFLOP/s"
+    else:
+        achieved, peak, unit = hbm_gbs, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
+                "kernel": "fwd_kernel" + ("+reduce_kernel" if split_keys(c) else ""),
+                "launch_ms_mean": round(run_ms, 5), "launch_ms_mean_warm": round(warm_run_ms, 5),
+                "plan_kernel_ms_mean_warm": round(plan_ms, 5), "algorithmic_flops": flops,
+                "algorithmic_bytes": alg_bytes, "mfma_tflops": round(mfma_tflops, 3),
+                "mfma_frac": round(mfma_tflops / peak_f, 4), "algorithmic_hbm_GBps": round(hbm_gbs, 1),
+                "hbm_frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
     value = flops / (ms_per_step * 1e-3) / 1e12
     res = {"metric": "HSTU fwd effective TFLOP/s (unmasked pairs) + % of bf16 MFMA peak, 1 GPU",
            "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": dtype, "data": "synthetic (seeded numpy draws, rounded to dtype)",
-           "config": dict(workload=name, **desc), "pct_of_mfma_peak": round(100 * value / peak, 2),
+           "config": dict(workload=name, **desc), "pct_of_mfma_peak": round(100 * value / peak_f, 2),
+           "timing": "cold: a 1 GiB device write before each step (outside the events) evicts L2 and Infinity "
+                     "Cache; per-step HIP events on the launch stream",
+           "ms_per_step_median": round(statistics.median(step_ms), 5),
+           "timed_region_wall_ms": round(region_wall_ms, 3),
+           "warm_ms_per_step": round(warm_step_ms, 5),
+           "warm_value": round(flops / (warm_step_ms * 1e-3) / 1e12, 3),
            "roofline": roofline}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(c, name, flops)
@@ -342,6 +551,9 @@ def main():
     args = parse()
     if args.traffic_record:
         traffic_record(*args.traffic_record)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary[0], args.counter_summary[1:])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library has no multi-GPU "

@@ -182,8 +182,9 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
     query and key lengths differ (queries are the last positions of each
     sequence). rab and mask are [B, Hq or 1, max_seq_len, max_seq_len].
     mask_type defaults to MASK_CUSTOM when a mask is given, else MASK_CAUSAL.
-    max_seq_len defaults to the longest key sequence (read back from the
-    device: pass it explicitly to avoid that synchronisation)."""
+    max_seq_len (the page's maximum sequence length: the row stride of rab
+    and mask, and the bound on every key sequence) is required: the binding
+    never reads device arrays back."""
     lib = load_library()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [tokens, heads, head_dim]")
@@ -201,8 +202,8 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
     if mask_type is None:
         mask_type = MASK_CUSTOM if mask is not None else MASK_CAUSAL
     if max_seq_len is None:
-        ko = off if offk is None else offk
-        max_seq_len = int((ko[1:] - ko[:-1]).max().item()) if B > 0 else 1
+        raise ValueError("max_seq_len is required")
+    max_seq_len = int(max_seq_len)
     if out_scale is None:
         out_scale = 1.0 / max_seq_len
     heads = {}
@@ -248,8 +249,8 @@ def prepare_fwd_paged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                       workspace: Optional[torch.Tensor] = None) -> Prepared:
     """Marshal a paged-KV forward. kv_cache [num_pages, 2, page_size, Hk, D].
 
-    max_seq_len (history + new tokens, per request) defaults to the value
-    read back from the device arrays."""
+    max_seq_len (the bound on history + new tokens of every request) is
+    required: the binding never reads device arrays back."""
     lib = load_library()
     device, dtype = q.device, q.dtype
     if dtype not in DTYPE_CODES:
@@ -265,11 +266,8 @@ def prepare_fwd_paged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     B = int(offq.shape[0]) - 1
     page_size = int(kv_cache.shape[2])
     if max_seq_len is None:
-        if B > 0:
-            npg = (poff[1:] - poff[:-1]).long()
-            hist = torch.where(npg > 0, (npg - 1) * page_size + lpl.long(), torch.zeros_like(npg))
-            max_seq_len = int((hist + (offq[1:] - offq[:-1]).long()).max().item())
-        max_seq_len = max(int(max_seq_len or 1), 1)
+        raise ValueError("max_seq_len is required")
+    max_seq_len = int(max_seq_len)
     if out_scale is None:
         out_scale = 1.0 / max_seq_len
     nc = _int32(num_context, "num_context", device)

@@ -13,6 +13,9 @@
 namespace {
 
 constexpr int32_t kMaxSeqLen = 20480;
+// The page's batch bound (B in [1, 2048]). The scheduler also relies on it:
+// a work-list entry packs the sequence index into 16 bits.
+constexpr int32_t kMaxBatch = 2048;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -40,6 +43,7 @@ hstu_status_t check_common(int32_t batch, int32_t max_seq_len, int32_t hq, int32
     return mask == 1 ? HSTU_ERR_UNSUPPORTED : HSTU_ERR_INVALID_ARG;
   }
   if (batch == 0 || hq == 0 || d == 0) return HSTU_OK;  // empty input: nothing runs
+  if (batch > kMaxBatch) return HSTU_ERR_INVALID_ARG;
   if (hk <= 0 || hq % hk != 0) return HSTU_ERR_INVALID_ARG;
   if (max_seq_len < 1 || max_seq_len > kMaxSeqLen) return HSTU_ERR_INVALID_ARG;
   if (!head_dim_ok(d, dtype)) return HSTU_ERR_UNSUPPORTED;
@@ -56,7 +60,7 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
                                int32_t head_dim, hstu_dtype_t dtype, int32_t is_delta_qk) {
   if (batch < 0 || max_seq_len < 0 || num_heads_q < 0 || num_heads_kv < 0 || head_dim < 0) return 0;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return 256;
-  if (num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
+  if (batch > kMaxBatch || num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
   return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype),
                                    is_delta_qk != 0);
 }
@@ -65,7 +69,7 @@ size_t hstu_fwd_paged_workspace_size(int32_t batch, int32_t page_size, int32_t m
                                      int32_t num_heads_kv, int32_t head_dim, hstu_dtype_t dtype) {
   if (page_size < 0 || batch < 0 || max_seq_len < 0 || num_heads_q < 0 || num_heads_kv < 0 || head_dim < 0) return 0;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return 256;
-  if (num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
+  if (batch > kMaxBatch || num_heads_kv == 0 || num_heads_q % num_heads_kv != 0 || !dtype_ok(dtype)) return 0;
   // New tokens per request are bounded by max_seq_len (history + new).
   return hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, to_internal(dtype), true);
 }

@@ -472,11 +472,15 @@ __device__ inline void leave_queue(const KParams& p) {
 // bf16 / fp16 forward
 //
 // LDS holds two buffers of one K tile and one V tile, both row-major
-// [BN keys][D features] with no padding; 16-byte chunk c of key row j sits
-// at chunk slot c ^ swz(j), so the MFMA operand reads below hit distinct
-// banks. Tiles arrive by global->LDS DMA (16 bytes per lane), so no
-// registers stage them. One barrier per tile: tile n+1 is requested right
-// after the barrier that publishes tile n, into the buffer tile n-1 used.
+// [BN keys][D features] with padded rows: a K row is followed by 16 bytes
+// and a V row stride is 64 bytes past a multiple of 256, so every MFMA
+// operand read below hits distinct banks with plain addresses (one base
+// register per lane and compile-time offsets). Tiles arrive by
+// global->LDS DMA (16 bytes per lane), so no registers stage them; the
+// padding slots receive a dummy load. One barrier per tile: tile n+1 is
+// requested right after the barrier that publishes tile n, into the buffer
+// tile n-1 used. (The output staging at the end of an item reuses these
+// buffers with unpadded rows and an XOR swizzle of 16-byte chunks, swz.)
 //
 // Q is pre-scaled by c = -alpha*log2(e) while it is loaded, so the MFMA
 // yields y = c*(Q.K) directly; with rab, y += c*rab. Then

@@ -44,6 +44,7 @@
  *    <= max_seq_len, page ids in range) is the caller's duty, as the page
  *    says for seq_offsets; it is not checked.
  *  - Return codes only; nothing is thrown across the ABI.
+ *  - batch is at most 2048 (the page's B range).
  *  - If batch, num_heads_q or head_dim is 0 the input is empty: the call
  *    returns HSTU_OK and launches nothing (the page's note on empty inputs).
  */
@@ -70,12 +71,13 @@ typedef enum { HSTU_F32 = 0, HSTU_F16 = 1, HSTU_BF16 = 2 } hstu_dtype_t;
 
 typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2, HSTU_MASK_CUSTOM = 3 } hstu_mask_t;
 
-/* Supported sizes: head_dim in {32, 64, 128, 256} for f16/bf16 and
- * {32, 64, 128} for f32 (the page allows multiples of 16 up to 512);
- * num_heads_q % num_heads_kv == 0 (the page's GQA rule); page_size in
- * {32, 64, 128, 256}; max_seq_len in [1, 20480]; rab and user-mask head
- * counts 1 or num_heads_q; the user mask (HSTU_MASK_CUSTOM) in f16/bf16
- * jagged calls. */
+/* Supported sizes: batch in [0, 2048] (the page's B range; larger batches
+ * return HSTU_ERR_INVALID_ARG and a workspace size of 0); head_dim in
+ * {32, 64, 128, 256} for f16/bf16 and {32, 64, 128} for f32 (the page
+ * allows multiples of 16 up to 512); num_heads_q % num_heads_kv == 0 (the
+ * page's GQA rule); page_size in {32, 64, 128, 256}; max_seq_len in
+ * [1, 20480]; rab and user-mask head counts 1 or num_heads_q; the user mask
+ * (HSTU_MASK_CUSTOM) in f16/bf16 jagged calls. */
 
 /*
  * Workspace bytes hstu_fwd needs for these sizes (the work list of the tile
@@ -96,8 +98,11 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
  *  rab           [batch, rab_num_heads, max_seq_len, max_seq_len] dtype, or
  *                NULL. rab_num_heads is num_heads_q or 1 (the page's rab
  *                broadcast [b, 1, s, s]: one rab for every head). Indexed by
- *                absolute positions (i, j) within the sequence; only (i, j)
- *                the mask does not remove are read.
+ *                absolute positions (i, j) within the sequence. Entries the
+ *                mask removes may be loaded (whole tile rows inside the
+ *                sequence are read) but never affect the output, even when
+ *                they hold NaN or inf; entries outside the sequence are
+ *                never read.
  *  mask          [batch, mask_num_heads, max_seq_len, max_seq_len] dtype with
  *                HSTU_MASK_CUSTOM, else NULL. mask_num_heads is num_heads_q or
  *                1; indexed as rab. f16/bf16 only.

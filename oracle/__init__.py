@@ -67,6 +67,8 @@ def _load():
     lib.hstu_oracle_fwd_paged.restype = ctypes.c_int
     lib.hstu_oracle_num_threads.argtypes = []
     lib.hstu_oracle_num_threads.restype = ctypes.c_int
+    lib.hstu_oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.hstu_oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -87,6 +89,11 @@ def _ptr(a: Optional[np.ndarray]):
 
 def num_threads() -> int:
     return int(_load().hstu_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing only)."""
+    _load().hstu_oracle_set_num_threads(int(n))
 
 
 def silu(x: float) -> float:

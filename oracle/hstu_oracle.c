@@ -224,10 +224,13 @@ int hstu_oracle_fwd_paged(const double* q, const double* k_new, const double* v_
   return err ? -1 : 0;
 }
 
-/* Number of threads OpenMP would use (reported by the CPU baseline). */
+/* Number of threads OpenMP would use (reported by the CPU baseline), and a
+ * setter for it (the baseline also times one thread). Not arithmetic. */
 #ifdef _OPENMP
 #include <omp.h>
 int hstu_oracle_num_threads(void) { return omp_get_max_threads(); }
+void hstu_oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int hstu_oracle_num_threads(void) { return 1; }
+void hstu_oracle_set_num_threads(int n) { (void)n; }
 #endif

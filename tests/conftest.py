@@ -10,9 +10,3 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-
-
-def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly (not skip) when the GPU is requested but missing;
-    # they are only deselected here when the run does not ask for them.
-    pass

@@ -78,6 +78,8 @@ def test_empty_inputs_are_a_noop(lib):
     (dict(Hk=3), INVAL),                      # Hq not a multiple of Hk
     (dict(Hk=0), INVAL),
     (dict(B=-1), INVAL),
+    (dict(B=2049), INVAL),                    # the page's B range; work-list entries pack b in 16 bits
+    (dict(B=40000), INVAL),
     (dict(g=-1), INVAL),
     (dict(S=0), INVAL),
     (dict(S=20481), INVAL),
@@ -119,6 +121,7 @@ def test_fwd_rejects(lib, kw, code):
     (dict(Hk=3), INVAL),
     (dict(mask=3), UNSUP),
     (dict(wsb=8), WS),
+    (dict(B=2049), INVAL),
 ])
 def test_paged_rejects(lib, kw, code):
     assert paged(lib, **kw) == code
@@ -134,8 +137,24 @@ def test_workspace_sizes(lib):
     assert hj.hstu_fwd_workspace_size(32, 2048, 4, 4, 128, __import__("torch").bfloat16, is_delta_qk=True) > \
         hj.hstu_fwd_workspace_size(32, 2048, 4, 4, 128, __import__("torch").bfloat16)
     assert lib.hstu_fwd_paged_workspace_size(64, 64, 4160, 4, 4, 128, BF16) > 0
+    # batches past the page's B range have no workspace size
+    assert lib.hstu_fwd_workspace_size(2048, 128, 4, 4, 128, BF16, 0) > 0
+    assert lib.hstu_fwd_workspace_size(2049, 128, 4, 4, 128, BF16, 0) == 0
+    assert lib.hstu_fwd_paged_workspace_size(2049, 64, 4160, 4, 4, 128, BF16) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         hj.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_requires_max_seq_len():
+    # The binding never reads device arrays back, so the page's maximum
+    # sequence length must be given (checked before anything is launched).
+    import torch
+    q = torch.zeros(4, 2, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="max_seq_len"):
+        hj.prepare_fwd(q, q, q, [0, 4])
+    kv = torch.zeros(1, 2, 32, 2, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="max_seq_len"):
+        hj.prepare_fwd_paged(q, q, q, kv, [0, 4], [0, 1], [0], [1])
