@@ -40,7 +40,7 @@ DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 # Every symbol include/hstu.h declares.
 EXPORTED = ("hstu_fwd_workspace_size", "hstu_fwd", "hstu_fwd_plan", "hstu_fwd_run", "hstu_fwd_paged_workspace_size",
-            "hstu_fwd_paged", "hstu_fwd_paged_plan", "hstu_fwd_paged_run", "hstu_status_string")
+            "hstu_fwd_paged", "hstu_fwd_paged_plan", "hstu_fwd_paged_run", "hstu_fwd_noalloc", "hstu_status_string")
 
 
 class HstuError(RuntimeError):
@@ -77,6 +77,8 @@ def load_library(path: Optional[str] = None):
     for name in ("hstu_fwd_paged", "hstu_fwd_paged_run"):
         getattr(lib, name).argtypes = pag
         getattr(lib, name).restype = E
+    lib.hstu_fwd_noalloc.argtypes = jag[:22] + [P]
+    lib.hstu_fwd_noalloc.restype = E
     lib.hstu_fwd_plan.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
     lib.hstu_fwd_plan.restype = E
     lib.hstu_fwd_paged_plan.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
@@ -144,6 +146,7 @@ class Prepared:
 
     def __init__(self, name: str, lib, fwd_args, plan_args, out: torch.Tensor, workspace: torch.Tensor, keep):
         self.name = name
+        self._lib = lib
         self._fwd = getattr(lib, name)
         self._run = getattr(lib, name + "_run")
         self._plan = getattr(lib, name + "_plan")
@@ -240,6 +243,20 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
 def hstu_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, **kw) -> torch.Tensor:
     """Jagged HSTU forward; returns out [T, Hq, D]. Keywords as prepare_fwd."""
     return prepare_fwd(q, k, v, seq_offsets, **kw).fwd()
+
+
+def hstu_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, *, out: torch.Tensor,
+                     **kw) -> torch.Tensor:
+    """hstu_fwd through the allocation-free entry point: the library uses its
+    static device scratch instead of a workspace, and the caller passes
+    ``out`` (integer side inputs must already be int32 device tensors for
+    the call itself to allocate nothing). Keywords as prepare_fwd."""
+    prep = prepare_fwd(q, k, v, seq_offsets, out=out, workspace=torch.empty(0, dtype=torch.uint8, device=q.device),
+                       **kw)
+    st = prep._lib.hstu_fwd_noalloc(*prep._fwd_args[:22], prep._fwd_args[24])
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_fwd_noalloc")
+    return out
 
 
 def prepare_fwd_paged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kv_cache: torch.Tensor,

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhstu.so")
-SOURCES = [os.path.join(CSRC, "hstu_kernels.hip"), os.path.join(CSRC, "hstu_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "hstu_kernels.hip"), os.path.join(CSRC, "hstu_scratch.hip"),
+           os.path.join(CSRC, "hstu_abi.cpp")]
 HEADERS = [os.path.join(ROOT, "include", "hstu.h"), os.path.join(CSRC, "hstu_internal.h")]
 
 ARCH = "gfx950"

@@ -88,12 +88,15 @@ hstu_status_t enqueue(const hstu::FwdArgs& a, int phase) {
 
 // Jagged entry points share this body. Pointers a run does not need (q, k,
 // v, out) may be NULL in the plan-only phase.
+// scratch: the workspace is the library's static device scratch (the
+// allocation-free entry point); its layout is then sized to fit it.
 hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, const void* rab, const void* mask,
                      void* out, const int32_t* seq_offsets, const int32_t* seq_offsets_k,
                      const int32_t* num_context, const int32_t* num_targets, int32_t batch, int32_t max_seq_len,
                      int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads,
                      int32_t mask_num_heads, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
-                     float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                     float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream,
+                     bool scratch = false) {
   hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
                                   target_group_size, dtype, num_context, num_targets);
   if (st != HSTU_OK) return st;
@@ -112,7 +115,10 @@ hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, con
     if (mask && mask_num_heads != 1 && mask_num_heads != num_heads_q) return HSTU_ERR_INVALID_ARG;
   }
   const size_t need =
-      hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, dtype, seq_offsets_k ? 1 : 0);
+      scratch ? hstu::fwd_workspace_bytes(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim,
+                                          to_internal(dtype), seq_offsets_k != nullptr, workspace_bytes)
+              : hstu_fwd_workspace_size(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, dtype,
+                                        seq_offsets_k ? 1 : 0);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return HSTU_ERR_WORKSPACE;
 
   hstu::FwdArgs a{};
@@ -142,6 +148,7 @@ hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, con
   a.out_scale = out_scale;
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
+  a.workspace_cap = scratch ? workspace_bytes : 0;
   a.stream = reinterpret_cast<hipStream_t>(stream);
   return enqueue(a, phase);
 }
@@ -216,6 +223,25 @@ hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* 
   return jagged(kBoth, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
                 max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
                 target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
+}
+
+hstu_status_t hstu_fwd_noalloc(const void* q, const void* k, const void* v, const void* rab, const void* mask,
+                               void* out, const int32_t* seq_offsets, const int32_t* seq_offsets_k,
+                               const int32_t* num_context, const int32_t* num_targets, int32_t batch,
+                               int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                               int32_t rab_num_heads, int32_t mask_num_heads, hstu_mask_t mask_type,
+                               int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
+                               void* stream) {
+  // Empty inputs and argument errors are reported before the scratch is touched.
+  hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
+                                  target_group_size, dtype, num_context, num_targets);
+  if (st != HSTU_OK || batch == 0 || num_heads_q == 0 || head_dim == 0) return st;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (hstu::scratch_workspace(&ws, &ws_bytes) != hipSuccess) return HSTU_ERR_HIP;
+  return jagged(kBoth, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
+                max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
+                target_group_size, alpha, out_scale, dtype, ws, ws_bytes, stream, true);
 }
 
 hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,

@@ -43,6 +43,7 @@ struct FwdArgs {
   float out_scale;
   void* workspace;
   size_t workspace_bytes;
+  size_t workspace_cap;  // 0, or the fixed size of the static scratch (see fwd_workspace_bytes)
   hipStream_t stream;
 };
 
@@ -50,8 +51,15 @@ struct FwdArgs {
 // the launch may split long items over the key range (split_keys: paged
 // calls and jagged calls with their own key offsets), the split list and
 // the fp32 partial sums.
+// cap > 0 sizes the layout for a workspace of at most cap bytes (fewer
+// partial-sum slots for split items); the result may still exceed cap.
 size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, DType dtype, bool split_keys);
+                           int32_t head_dim, DType dtype, bool split_keys, size_t cap = 0);
+
+// The static device scratch of the allocation-free entry point on the
+// current device: *ptr receives its device address (taken once per device
+// with hipGetSymbolAddress), *bytes its size. Allocates nothing.
+hipError_t scratch_workspace(void** ptr, size_t* bytes);
 
 // Enqueues the planner on args.stream: it writes the work list into the
 // workspace and zeroes the work-queue counters.

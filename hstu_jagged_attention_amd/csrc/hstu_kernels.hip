@@ -1538,30 +1538,47 @@ constexpr int kSplitUnits = 1024;  // (slot, head group) pairs of partial sums
 // path on the measured workloads, so they are not split.
 bool use_split(bool split_keys, DType dtype) { return split_keys && dtype != DType::F32; }
 
+// cap > 0: a workspace of at most cap bytes (the static scratch of the
+// allocation-free entry point). Split items then get as many partial-sum
+// slots as fit, at least 2; the planner picks longer key chunks when slots
+// are few, so the result stays correct (only the chunking changes).
 WsLayout ws_layout(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                   DType dtype, bool split_keys) {
+                   DType dtype, bool split_keys, size_t cap = 0) {
   WsLayout w{};
   const int group = num_heads_q / num_heads_kv;
   const int hpw_log2 = heads_per_wg_log2(group);
   const int bm = kRowsPerWave * (kWaves >> hpw_log2);
   w.n_hg = num_heads_q >> hpw_log2;
   w.n_qt_max = (max_q_len + bm - 1) / bm;
-  w.split_slots = use_split(split_keys, dtype) ? max(2, kSplitUnits / w.n_hg) : 0;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t entries = (size_t)batch * w.n_qt_max + w.split_slots;
-  w.items = kHeaderBytes;
-  w.splits = up(w.items + entries * 2 * sizeof(int32_t));
-  w.partials = up(w.splits + (size_t)w.split_slots * 2 * sizeof(int32_t));
-  w.total = w.partials + (size_t)w.split_slots * w.n_hg * kWaves * kRowsPerWave * head_dim * sizeof(float);
+  auto fill = [&](int slots) {
+    w.split_slots = slots;
+    const size_t entries = (size_t)batch * w.n_qt_max + slots;
+    w.items = kHeaderBytes;
+    w.splits = up(w.items + entries * 2 * sizeof(int32_t));
+    w.partials = up(w.splits + (size_t)slots * 2 * sizeof(int32_t));
+    w.total = w.partials + (size_t)slots * w.n_hg * kWaves * kRowsPerWave * head_dim * sizeof(float);
+  };
+  int slots = use_split(split_keys, dtype) ? max(2, kSplitUnits / w.n_hg) : 0;
+  fill(slots);
+  if (cap > 0 && w.total > cap && slots > 2) {
+    int lo = 2, hi = slots;  // total grows with the slot count: the largest count that fits
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      fill(mid);
+      if (w.total <= cap) lo = mid; else hi = mid - 1;
+    }
+    fill(lo);
+  }
   return w;
 }
 
 }  // namespace
 
 size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q, int32_t num_heads_kv,
-                           int32_t head_dim, DType dtype, bool split_keys) {
+                           int32_t head_dim, DType dtype, bool split_keys, size_t cap) {
   if (batch < 0 || max_q_len < 0 || num_heads_q <= 0 || num_heads_kv <= 0 || head_dim <= 0) return 0;
-  return ws_layout(batch, max_q_len, num_heads_q, num_heads_kv, head_dim, dtype, split_keys).total;
+  return ws_layout(batch, max_q_len, num_heads_q, num_heads_kv, head_dim, dtype, split_keys, cap).total;
 }
 
 namespace {
@@ -1585,7 +1602,7 @@ KParams make_params(const FwdArgs& a) {
   p.page_ids = a.page_ids;
   p.last_page_len = a.last_page_len;
   const WsLayout w = ws_layout(a.batch, a.max_seq_len, a.num_heads_q, a.num_heads_kv, a.head_dim, a.dtype,
-                               a.paged || a.seq_offsets_k != nullptr);
+                               a.paged || a.seq_offsets_k != nullptr, a.workspace_cap);
   char* ws = (char*)a.workspace;
   p.n_items = (int32_t*)ws;
   p.counter = (int32_t*)(ws + 64);

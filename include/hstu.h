@@ -221,6 +221,30 @@ hstu_status_t hstu_fwd_paged_run(const void* q, const void* k_new, const void* v
                                  int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
                                  void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
 
+/*
+ * hstu_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. Arguments, results and errors are those
+ * of hstu_fwd. The tile scheduler's work list, queue counters and partial
+ * sums live in a static 16 MiB array of the library's own device memory
+ * (one per GPU, held until the process ends; its address is taken once per
+ * device). The call allocates nothing and frees nothing. The stream must
+ * belong to the current device. Calls with separate key offsets get as
+ * many partial-sum slots as fit, so their key chunks may be longer than
+ * hstu_fwd's (same results up to fp32 summation order). Sizes whose work
+ * list does not fit (in practice batch * ceil(max_seq_len / rows per item)
+ * beyond about 2 million entries) return HSTU_ERR_WORKSPACE. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.
+ */
+hstu_status_t hstu_fwd_noalloc(const void* q, const void* k, const void* v, const void* rab, const void* mask,
+                               void* out, const int32_t* seq_offsets, const int32_t* seq_offsets_k,
+                               const int32_t* num_context, const int32_t* num_targets, int32_t batch,
+                               int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                               int32_t rab_num_heads, int32_t mask_num_heads, hstu_mask_t mask_type,
+                               int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
+                               void* stream /* hipStream_t */);
+
 /* Static description of a status code. Never NULL. */
 const char* hstu_status_string(hstu_status_t status);
 

@@ -1,0 +1,60 @@
+"""The allocation-free entry point (hstu_fwd_noalloc) through the C ABI,
+against hstu_fwd on the same inputs: two calls in a row on one GPU, the
+second with a smaller input, so the static scratch is reused with the last
+call's contents still in it. Calls whose scratch layout equals hstu_fwd's
+workspace layout run the same kernels on the same work list and must agree
+bit for bit; calls with separate key offsets get fewer partial-sum slots
+(longer key chunks), so they are compared element by element with the
+oracle at the stated tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import hstu_jagged_attention_amd as hj
+from hstu_jagged_attention_amd import workloads as wl
+from _helpers import assert_parity, gpu_device, oracle_jagged, run_jagged
+
+pytestmark = pytest.mark.gpu
+
+
+def _noalloc(c, dev):
+    out = torch.full(tuple(c.q.shape), float("nan"), dtype=c.q.dtype, device=dev)
+    kw = dict(rab=None if c.rab is None else c.rab.to(dev), mask=None if c.mask is None else c.mask.to(dev),
+              seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
+              num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
+              mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
+    return hj.hstu_fwd_noalloc(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets), out=out, **kw)
+
+
+def test_noalloc_matches_hstu_fwd_twice_second_smaller():
+    dev = gpu_device()
+    big = wl.jagged_case(501, np.resize([0, 1, 31, 33, 65, 127, 129, 300, 257], 120), 8, 2, 128, "f16",
+                         num_context=(0, 12), num_targets=(0, 40), target_group_size=1, rab_std=0.3, max_seq_len=300,
+                         name="noalloc_big")
+    small = wl.jagged_case(502, [70, 1, 130], 4, 4, 64, "bf16", num_targets=(1, 9), target_group_size=2,
+                           max_seq_len=130, name="noalloc_small")
+    for c in (big, small):
+        print("[case]", c.name, "batch", c.batch, flush=True)
+        ref = run_jagged(c, dev)
+        got = _noalloc(c, dev)
+        torch.cuda.synchronize(dev)
+        assert torch.equal(got, ref), c.name
+        assert_parity(got, oracle_jagged(c), c.dtype, c.name)
+
+
+def test_noalloc_key_split_calls_twice_second_smaller():
+    dev = gpu_device()
+    lk = [500 + 13 * i for i in range(48)]
+    lq = [1 + (5 * i) % 64 for i in range(48)]
+    big = wl.jagged_case(503, lk, 4, 4, 128, "bf16", num_targets=lq, target_group_size=1, q_lengths=lq,
+                         name="noalloc_delta_big")
+    small = wl.jagged_case(504, [300, 129], 8, 2, 64, "bf16", mask_type=wl.MASK_NONE, q_lengths=[64, 129],
+                           name="noalloc_delta_small")
+    for c in (big, small):
+        print("[case]", c.name, "batch", c.batch, flush=True)
+        ref = run_jagged(c, dev)
+        got = _noalloc(c, dev)
+        torch.cuda.synchronize(dev)
+        o = oracle_jagged(c)
+        assert_parity(ref, o, c.dtype, c.name + " hstu_fwd")
+        assert_parity(got, o, c.dtype, c.name + " hstu_fwd_noalloc")
