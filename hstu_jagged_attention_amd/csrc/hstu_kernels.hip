@@ -44,6 +44,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <cmath>
 #include <type_traits>
 
 #include "hstu_internal.h"
@@ -108,6 +109,8 @@ struct KParams {
   int32_t mask_heads;
   float alpha;
   float c_exp;        // -alpha * log2(e)
+  float c_q;          // scale applied to Q as it is loaded (16-bit kernels): c_exp / y_mul
+  float y_mul;        // 1, or the power of two that restores c_exp (fp16 with |c_exp| > 1)
   float out_mul;      // final scale of O (see the kernels)
 };
 
@@ -482,11 +485,15 @@ __device__ inline void leave_queue(const KParams& p) {
 // tile n-1 used. (The output staging at the end of an item reuses these
 // buffers with unpadded rows and an XOR swizzle of 16-byte chunks, swz.)
 //
-// Q is pre-scaled by c = -alpha*log2(e) while it is loaded, so the MFMA
-// yields y = c*(Q.K) directly; with rab, y += c*rab. Then
+// Q is pre-scaled by c = -alpha*log2(e) while it is loaded (rounded to the
+// input dtype), so the MFMA yields y = c*(Q.K) directly; with rab,
+// y += c*rab. Then
 //   silu(alpha*s) = -(y / (1 + 2^y)) / log2(e),
 // and the constant -1/log2(e) joins out_scale in the final store, leaving
-// exp2, add, rcp, mul and a packed convert per element.
+// exp2, add, rcp, mul and a packed convert per element. In fp16, c*Q could
+// overflow when |c| > 1; Q is then scaled by c / 2^k (|c / 2^k| <= 1, so
+// |c Q / 2^k| <= |Q| stays finite) and S by the exact power of two 2^k
+// (y_mul) before the epilogue, in a block that is skipped when y_mul == 1.
 // ------------------------------------------------------------------------
 // Chunk-slot swizzle of key row j. For D = 128 (16 chunks of 16 bytes, one
 // row = all 64 banks) it is 4 (j % 4) + (j / 4) % 4: the 16 rows a 16-lane
@@ -753,7 +760,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         const V8 raw = __builtin_bit_cast(V8, x);
         V8 sc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = (T)((float)raw[e] * p.c_exp);
+        for (int e = 0; e < 8; ++e) sc[e] = (T)((float)raw[e] * p.c_q);
         qf[ks] = sc;
       }
     }
@@ -884,6 +891,13 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       }
       f32x16_t sacc[NJB];
       V8 pf[NJB][2];
+      // S block jb times y_mul (only when Q was scaled by c / y_mul).
+      auto scale_s = [&](int jb) {
+        if (p.y_mul != 1.f) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[jb][r] *= p.y_mul;
+        }
+      };
       // Epilogue of element r of block jb: rab, mask (masked tiles), SiLU, round.
       // rab and mask of element r of block jb: y (kept in sacc).
       // Element r of block jb of a prefetched rab / mask tile, as float.
@@ -963,6 +977,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         // selects one of two straight-line copies.
         auto body = [&](auto masked) {
           auto s_block = [&](int jb) {
+            if (jb > 0) scale_s(jb - 1);
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
             V8 kf = k_frag(jb, 0);
@@ -996,6 +1011,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
           };
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb) s_block(jb);
+          scale_s(NJB - 1);
           if (NJB > 1) {
             pv_block(0, true);
           } else {
@@ -1057,6 +1073,8 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int e = 0; e < GP; ++e) vf[0][e] = p_vf(e);
         auto epi_all = [&](auto masked) {
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb) scale_s(jb);
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb) epi_block(masked, jb);
         };
@@ -1583,6 +1601,7 @@ size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q
 
 namespace {
 
+
 KParams make_params(const FwdArgs& a) {
   KParams p = {};
   p.q = a.q;
@@ -1631,6 +1650,14 @@ KParams make_params(const FwdArgs& a) {
   // multiplies by s and folds alpha into the output scale; the 16-bit kernel
   // multiplies by y = c s (Q pre-scaled) and folds -1/log2(e) instead.
   p.c_exp = -a.alpha * kLog2e;
+  p.c_q = p.c_exp;
+  p.y_mul = 1.f;
+  if (a.dtype == DType::F16 && std::fabs(p.c_exp) > 1.f) {
+    int k = 0;
+    std::frexp(p.c_exp, &k);  // |c_exp| = m 2^k, m in [0.5, 1)
+    p.y_mul = std::ldexp(1.f, k);
+    p.c_q = std::ldexp(p.c_exp, -k);
+  }
   p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : -a.out_scale / kLog2e;
   const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256;
   // One chunk per two resident workgroups: measured against 4x, 2x, 1/2x and
@@ -1641,6 +1668,7 @@ KParams make_params(const FwdArgs& a) {
 }
 
 int tile_n(const FwdArgs& a) { return (a.dtype != DType::F32 && a.head_dim >= 256) ? 32 : 64; }
+
 
 // Items a run may have: (sequence, q tile, head group) plus split chunks.
 long long item_bound(const FwdArgs& a, const KParams& p) {

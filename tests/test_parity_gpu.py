@@ -164,6 +164,88 @@ def test_work_list_path_edge_mix(dev, case):
     assert_parity(got, oracle_jagged(c), dtype, name)
 
 
+# Work-list batches of 60 sequences with lengths from 0 to 700 (ragged tails
+# around every tile boundary) over every mask kind, GQA groups 4, 2 and 1
+# and head_dim 64 / 128, element by element.
+WORK_LIST_MIX = [
+    # (name, Hq, Hk, D, dtype, mask, nc, nt, g)
+    ("gqa4_f16_d128_ctx_targets_g1", 8, 2, 128, "f16", CAUSAL, (0, 40), (0, 70), 1),
+    ("gqa4_bf16_d128_targets_g3", 4, 1, 128, "bf16", CAUSAL, None, (1, 90), 3),
+    ("gqa4_f16_d64_targets_g0", 8, 2, 64, "f16", CAUSAL, (0, 20), (0, 50), 0),
+    ("gqa2_bf16_d128_causal", 4, 2, 128, "bf16", CAUSAL, None, None, 0),
+    ("mha_bf16_d128_ctx_targets", 2, 2, 128, "bf16", CAUSAL, (0, 30), (1, 40), 1),
+    ("mha_f16_d64_bidirectional", 2, 1, 64, "f16", NONE, None, None, 0),
+    ("gqa4_bf16_d128_bidirectional", 8, 2, 128, "bf16", NONE, None, None, 0),
+]
+TG_LENGTHS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 300, 511, 513, 700]
+
+
+@pytest.mark.parametrize("case", WORK_LIST_MIX, ids=[e[0] for e in WORK_LIST_MIX])
+def test_work_list_ragged_mask_mix(dev, case):
+    name, Hq, Hk, D, dtype, mask, nc, nt, g = case
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    lengths = rng.permutation(np.resize(np.array(TG_LENGTHS), 60))
+    c = wl.jagged_case(zlib.crc32(name.encode()) % (1 << 30), lengths, Hq, Hk, D, dtype, mask_type=mask,
+                       num_context=nc, num_targets=nt, target_group_size=g, max_seq_len=700, name=name)
+    group = Hq // Hk
+    hpw = 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+    items_4w = c.batch * -(-c.max_seq_len // (32 * (4 // hpw))) * (Hq // hpw)
+    assert items_4w > torch.cuda.get_device_properties(dev).multi_processor_count, "case must take the work-list path"
+    say(name, "batch", c.batch, "items", items_4w)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), dtype, name)
+
+
+def test_gqa_work_list_graph_replay_and_determinism(dev):
+    """The GQA work-list run's queue counters survive graph replays, and
+    runs are bitwise deterministic."""
+    c = wl.fp16_gqa_causal(batch=3)
+    say("gqa work-list graph", c.lengths.tolist())
+    s = torch.cuda.Stream(dev)
+    with torch.cuda.stream(s):
+        prep = _prepare(c, dev)
+        prep.plan()
+        prep.run()
+        s.synchronize()
+        eager = prep.out.clone()
+        prep.run()
+        s.synchronize()
+        assert torch.equal(prep.out, eager)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            prep.plan()
+            prep.run()
+        for _ in range(3):
+            prep.out.zero_()
+            g.replay()
+            s.synchronize()
+            assert torch.equal(prep.out, eager)
+    assert_parity(eager, oracle_jagged(c), c.dtype, "gqa work-list graph")
+
+
+@pytest.mark.parametrize("batch", [2, 40])
+def test_fp16_large_q_alpha_one(dev, batch):
+    """fp16 with alpha = 1 and |q| entries near 6e4 (small k): alpha*log2(e)*q
+    exceeds fp16's range, so Q is pre-scaled by c / 2^k and S restored by
+    2^k; the result must match the oracle (no overflow to inf). batch 2 runs
+    the direct key-split kernel, batch 40 the work-list kernel."""
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(40, 300, size=batch)
+    c = wl.jagged_case(78 + batch, lengths, 4, 4, 64, "f16", num_targets=(1, 9), target_group_size=1,
+                       max_seq_len=300, name="large_q")
+    q = c.q.float()
+    big = torch.as_tensor(rng.uniform(5e4, 6.5e4, size=q.shape), dtype=torch.float32)
+    sign = torch.as_tensor(rng.choice([-1.0, 1.0], size=q.shape), dtype=torch.float32)
+    pick = torch.as_tensor(rng.random(q.shape) < 0.05)
+    c.q = torch.where(pick, big * sign, q).half()
+    c.k = (c.k.float() * 1e-4).half()
+    c.alpha = 1.0
+    say("large |q| fp16 alpha 1, batch", batch)
+    got = run_jagged(c, dev)
+    assert torch.isfinite(got.float()).all()
+    assert_parity(got, oracle_jagged(c), "f16", "large q")
+
+
 def test_every_row_is_written(dev):
     c = wl.jagged_case(5, [45, 0, 200, 1], 4, 2, 128, "bf16", num_targets=(1, 9), target_group_size=1)
     say("every_row_is_written")
