@@ -25,7 +25,10 @@ MASK_CAUSAL = 0
 MASK_NONE = 2
 MASK_CUSTOM = 3
 
-TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+# rab and the user mask of an FP8 case are bf16 (the FP8 cast quantizes the
+# operands of the two products only).
+SIDE_DTYPES = {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8": "bf16"}
 
 IntSpec = Union[None, int, Sequence[int], tuple]
 
@@ -190,11 +193,11 @@ def jagged_case(seed: int, lengths: Sequence[int], num_heads_q: int, num_heads_k
         x *= np.float32(rab_std)
         if rab_padding_nan:
             padded_nan(x)
-        rab = torch.from_numpy(x).to(TORCH_DTYPES[dtype])
+        rab = torch.from_numpy(x).to(TORCH_DTYPES[SIDE_DTYPES[dtype]])
     mask = None
     if mask_keep is not None:
         m = (rng.random(size=(B, mask_heads or num_heads_q, S, S), dtype=np.float32) < mask_keep).astype(np.float32)
-        mask = torch.from_numpy(padded_nan(m)).to(TORCH_DTYPES[dtype])
+        mask = torch.from_numpy(padded_nan(m)).to(TORCH_DTYPES[SIDE_DTYPES[dtype]])
     return JaggedCase(name=name, dtype=dtype, q=q, k=k, v=v, rab=rab, seq_offsets=offsets_q, num_context=nc,
                       num_targets=nt, max_seq_len=S, mask_type=mask_type, target_group_size=target_group_size,
                       alpha=float(alpha if alpha is not None else 1.0 / math.sqrt(head_dim)),
@@ -294,6 +297,19 @@ def fp16_gqa_causal(seed: int = 4, batch: int = 16) -> JaggedCase:
                        name="fp16_gqa_causal")
 
 
+def fp8_gqa_causal(seed: int = 8, batch: int = 16) -> JaggedCase:
+    """The FP8 cast row on the GQA causal shape: as fp16_gqa_causal (batch
+    16, lognormal lengths median 1500 clipped to [128, 4096], 8 query heads
+    on 2 kv heads, d 128, causal, num_targets ~ U{1..32}, group size 1,
+    alpha 1/sqrt(128), out_scale 1/4096) with Q, K, V drawn N(0, 1) and
+    cast to OCP E4M3 (FN); the output is bf16."""
+    rng = np.random.default_rng(seed)
+    lengths = np.clip(np.round(rng.lognormal(math.log(1500.0), 0.5, size=batch)), 128, 4096).astype(np.int64)
+    return jagged_case(seed + 1000, lengths, 8, 2, 128, "fp8", mask_type=MASK_CAUSAL, num_targets=(1, 32),
+                       target_group_size=1, max_seq_len=4096, alpha=1.0 / math.sqrt(128), out_scale=1.0 / 4096,
+                       name="fp8_gqa_causal")
+
+
 def bf16_paged_target(seed: int = 5, batch: int = 64) -> PagedCase:
     """64 requests, cached history ~ U{512..4096} in 64-token pages under a
     seeded shuffled block table, 1..64 new target tokens as queries
@@ -340,4 +356,5 @@ WORKLOADS: Dict[str, Callable[..., object]] = {
     "bf16_paged_target": bf16_paged_target,
     "bf16_custom_mask": bf16_custom_mask,
     "bf16_delta_qk": bf16_delta_qk,
+    "fp8_gqa_causal": fp8_gqa_causal,
 }

@@ -59,8 +59,10 @@ def _load():
     lib.hstu_oracle_vis.restype = ctypes.c_int
     lib.hstu_oracle_mask.argtypes = [I32, I64, I64, I64, I64, P]
     lib.hstu_oracle_mask.restype = None
+    lib.hstu_oracle_e4m3.argtypes = [D]
+    lib.hstu_oracle_e4m3.restype = D
     lib.hstu_oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I64, D, D,
-                                    P, I64]
+                                    I32, P, I64]
     lib.hstu_oracle_fwd.restype = ctypes.c_int
     lib.hstu_oracle_fwd_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I64, D, D,
                                           P, I64]
@@ -100,6 +102,11 @@ def silu(x: float) -> float:
     return float(_load().hstu_oracle_silu(float(x)))
 
 
+def e4m3(x: float) -> float:
+    """x cast to OCP E4M3 (FN): nearest, ties to even, saturating at +-448."""
+    return float(_load().hstu_oracle_e4m3(float(x)))
+
+
 def vis(mask_type: int, L: int, nc: int, nt: int, g: int, i: int, j: int) -> bool:
     return bool(_load().hstu_oracle_vis(mask_type, L, nc, nt, g, i, j))
 
@@ -113,12 +120,15 @@ def mask_matrix(mask_type: int, L: int, nc: int = 0, nt: int = 0, g: int = 0) ->
 
 def hstu_fwd(q, k, v, seq_offsets, *, rab=None, mask=None, seq_offsets_k=None, num_context=None,
              num_targets=None, max_seq_len: int, mask_type: int = MASK_CAUSAL, target_group_size: int = 0,
-             alpha: float = 1.0, out_scale: Optional[float] = None, rows: Optional[Sequence] = None) -> np.ndarray:
+             alpha: float = 1.0, out_scale: Optional[float] = None, rows: Optional[Sequence] = None,
+             p_fp8: bool = False) -> np.ndarray:
     """Jagged forward in float64.
 
     q [Tq, Hq, D], k/v [Tk, Hk, D]; seq_offsets for q and seq_offsets_k for
     k/v (None: the same). rab [B, Hq or 1, max_seq_len, max_seq_len] or None;
     mask (mask_type 3 only) [B, Hq or 1, max_seq_len, max_seq_len].
+    p_fp8: the FP8 cast, P cast to E4M3 before the product with V (the
+    inputs are then E4M3 values, passed widened).
     Returns out [Tq, Hq, D], or [len(rows), D] when ``rows`` lists (token, head) pairs.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -143,7 +153,7 @@ def hstu_fwd(q, k, v, seq_offsets, *, rab=None, mask=None, seq_offsets_k=None, n
     rc = _load().hstu_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rab_a), _ptr(mask_a), _ptr(out), _ptr(off),
                                  _ptr(offk), _ptr(nc), _ptr(nt), B, max_seq_len, Hq, Hk, D,
                                  1 if rab_a is None else rab_a.shape[1], 1 if mask_a is None else mask_a.shape[1],
-                                 mask_type, target_group_size, float(alpha), float(out_scale),
+                                 mask_type, target_group_size, float(alpha), float(out_scale), int(bool(p_fp8)),
                                  _ptr(rows_a), 0 if rows_a is None else rows_a.shape[0])
     if rc != 0:
         raise ValueError("oracle: invalid arguments")

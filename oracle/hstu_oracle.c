@@ -41,7 +41,13 @@
  *   - mask_type 3 (user mask, the table's mask input [B, N, S, S]): every key
  *     of the sequence is a candidate and the mask value m = mask[b,h,i,j]
  *     multiplies P; m == 0 removes the key entirely (it contributes exactly
- *     zero, whatever the score), as the built-in masks do.
+ *     zero, whatever the score), as the built-in masks do;
+ *   - FP8 "cast" (the feature table's FP8 quantization row): element-level
+ *     quantization with no scale. Q, K and V arrive as OCP E4M3 (FN) values
+ *     (callers pass them widened to float64), and P = silu(...) is cast to
+ *     E4M3 before the product with V: round to nearest, ties to even, on the
+ *     E4M3 grid (3 mantissa bits, exponent bias 7, subnormal step 2^-9),
+ *     saturating to +-448 beyond the largest finite value (p_fp8 = 1).
  *
  * Every function is a direct loop over the definition; no blocking, no
  * reordering beyond summation order in j and e.
@@ -57,6 +63,23 @@
 
 /* SiLU, textbook form x * sigmoid(x). */
 double hstu_oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* The OCP E4M3 (FN) value nearest to x, ties to even, saturating at +-448.
+ * E4M3 holds sign * 2^(e-7) * (1 + m/8) for biased exponents e = 1..15
+ * (the top code 0x7f is NaN, so the largest finite value is 1.75 * 2^8 =
+ * 448) and sign * m * 2^-9 for e = 0: for |x| >= 2^-6 the grid step is
+ * 2^(floor(log2 |x|) - 3), below it 2^-9. */
+double hstu_oracle_e4m3(double x) {
+  if (x != x) return x;
+  const double a = fabs(x);
+  if (a >= 448.0) return x < 0 ? -448.0 : 448.0;
+  int e2 = 0;
+  (void)frexp(a, &e2); /* a = f 2^e2, f in [0.5, 1): floor(log2 a) = e2 - 1 */
+  const double step = (a >= ldexp(1.0, -6)) ? ldexp(1.0, e2 - 1 - 3) : ldexp(1.0, -9);
+  double r = nearbyint(a / step) * step; /* the default rounding mode: nearest, ties to even */
+  if (r > 448.0) r = 448.0;
+  return x < 0 ? -r : r;
+}
 
 /* Visibility of key j to query i, both positions local to one sequence of
  * length L, under the reading stated in the header comment. */
@@ -85,7 +108,7 @@ static void one_row(const double* qrow, const double* const* krows, const double
                     const double* rabrow /* nullable, indexed by local j */,
                     const double* maskrow /* nullable (mask_type 3), indexed by local j */, int64_t L, int64_t D,
                     int32_t mask_type, int64_t nc, int64_t nt, int64_t g, int64_t i, double alpha, double out_scale,
-                    double* out) {
+                    int32_t p_fp8, double* out) {
   for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
   for (int64_t j = 0; j < L; ++j) {
     if (!hstu_oracle_vis(mask_type, L, nc, nt, g, i, j)) continue;
@@ -94,6 +117,7 @@ static void one_row(const double* qrow, const double* const* krows, const double
     for (int64_t e = 0; e < D; ++e) s += qrow[e] * krows[j][e];
     if (rabrow) s += rabrow[j];
     double p = hstu_oracle_silu(alpha * s);
+    if (p_fp8) p = hstu_oracle_e4m3(p); /* FP8 cast of P before the product with V */
     if (maskrow) p *= maskrow[j];
     for (int64_t d = 0; d < D; ++d) out[d] += p * vrows[j][d];
   }
@@ -108,6 +132,7 @@ static void one_row(const double* qrow, const double* const* krows, const double
  *   out [Tq, Hq, D]
  *   seq_offsets [B+1] (queries); seq_offsets_k [B+1] (keys) or NULL (same);
  *   num_context, num_targets [B] or NULL.
+ * p_fp8 != 0: P is cast to E4M3 before the product with V (FP8 cast).
  * If rows != NULL, only the n_rows (token, head) pairs listed in rows[2*r],
  * rows[2*r+1] are computed, into out[r*D ...] (sampled mode); otherwise all.
  * Returns 0 on success, -1 on invalid arguments.
@@ -116,7 +141,7 @@ int hstu_oracle_fwd(const double* q, const double* k, const double* v, const dou
                     double* out, const int64_t* seq_offsets, const int64_t* seq_offsets_k,
                     const int64_t* num_context, const int64_t* num_targets, int64_t B, int64_t max_seq_len, int64_t Hq,
                     int64_t Hk, int64_t D, int64_t rab_heads, int64_t mask_heads, int32_t mask_type, int64_t g,
-                    double alpha, double out_scale, const int64_t* rows, int64_t n_rows) {
+                    double alpha, double out_scale, int32_t p_fp8, const int64_t* rows, int64_t n_rows) {
   if (B < 0 || Hq <= 0 || Hk <= 0 || D <= 0 || Hq % Hk != 0) return -1;
   if ((mask_type == ORACLE_MASK_CUSTOM) != (mask != NULL)) return -1;
   if (rab && rab_heads != 1 && rab_heads != Hq) return -1;
@@ -158,7 +183,7 @@ int hstu_oracle_fwd(const double* q, const double* k, const double* v, const dou
     const int64_t hr = rab_heads == 1 ? 0 : h, hm = mask_heads == 1 ? 0 : h;
     const double* rabrow = rab ? rab + ((b * rab_heads + hr) * max_seq_len + i) * max_seq_len : NULL;
     const double* maskrow = mask ? mask + ((b * mask_heads + hm) * max_seq_len + i) * max_seq_len : NULL;
-    one_row(q + (t * Hq + h) * D, kr, vr, rabrow, maskrow, L, D, mask_type, nc, nt, g, i, alpha, out_scale, o);
+    one_row(q + (t * Hq + h) * D, kr, vr, rabrow, maskrow, L, D, mask_type, nc, nt, g, i, alpha, out_scale, p_fp8, o);
     free(kr);
     free(vr);
   }
@@ -217,7 +242,7 @@ int hstu_oracle_fwd_paged(const double* q, const double* k_new, const double* v_
       kr[Lh + j] = k_new + ((q0 + j) * Hk + hk) * D;
       vr[Lh + j] = v_new + ((q0 + j) * Hk + hk) * D;
     }
-    one_row(q + (t * Hq + h) * D, kr, vr, NULL, NULL, L, D, mask_type, nc, nt, g, i, alpha, out_scale, o);
+    one_row(q + (t * Hq + h) * D, kr, vr, NULL, NULL, L, D, mask_type, nc, nt, g, i, alpha, out_scale, 0, o);
     free(kr);
     free(vr);
   }

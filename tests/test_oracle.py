@@ -624,3 +624,118 @@ def test_general_oracle_rejects_bad_arguments():
     d = wl.jagged_case(29, [4, 6], 2, 2, 8, "f32", alpha=0.7, out_scale=0.3)
     with pytest.raises(ValueError):  # more queries than keys
         oracle.hstu_fwd(f64(d.q), f64(d.k)[:8], f64(d.v)[:8], d.seq_offsets, seq_offsets_k=[0, 3, 8], max_seq_len=6)
+
+
+# ---------------------------------------------------------------- FP8 cast (row f3)
+E4M3 = torch.float8_e4m3fn
+
+
+def torch_e4m3(x):
+    """torch's own E4M3 (FN) cast of float32 values: round to nearest, ties to
+    even (NaN past the range, which the pins below stay inside)."""
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(E4M3).to(torch.float64).numpy()
+
+
+def all_e4m3_values():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(E4M3).to(torch.float64).numpy()
+    return vals[np.isfinite(vals)]
+
+
+def test_e4m3_every_code_maps_to_itself():
+    vals = all_e4m3_values()
+    assert vals.size == 254 and vals.max() == 448.0 and vals.min() == -448.0
+    for v in vals:
+        assert oracle.e4m3(float(v)) == v
+
+
+def test_e4m3_matches_library_cast():
+    rng = np.random.default_rng(0)
+    mag = np.exp(rng.uniform(np.log(1e-4), np.log(463.0), size=20000)).astype(np.float32)
+    x = (mag * rng.choice([-1.0, 1.0], size=mag.size)).astype(np.float32)
+    # exact midpoints between neighbouring codes (ties to even) and points just beside them
+    vals = np.unique(all_e4m3_values())
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, np.nextafter(mids, np.float32(1e4)), np.nextafter(mids, np.float32(-1e4))])
+    x = x[np.abs(x) < 464.0]
+    got = np.array([oracle.e4m3(float(t)) for t in x])
+    np.testing.assert_array_equal(got, torch_e4m3(x))
+
+
+def test_e4m3_hand_values_and_saturation():
+    # ties to even on the grid; subnormal step 2^-9; saturation beyond 448 (the stated reading)
+    cases = {1.0625: 1.0, 1.1875: 1.25, 0.3: 0.3125, -2.7: -2.75, 2.0 ** -10: 0.0, 3 * 2.0 ** -10: 2.0 ** -8,
+             0.001: 2.0 ** -9, 17.0: 16.0, 447.0: 448.0, 460.0: 448.0, 464.0: 448.0, 500.0: 448.0, 1e6: 448.0,
+             -1e6: -448.0, 0.0: 0.0}
+    for x, want in cases.items():
+        assert oracle.e4m3(x) == want, (x, oracle.e4m3(x), want)
+    assert math.isnan(oracle.e4m3(float("nan")))
+
+
+def fp8_case(seed, lengths, Hq=2, Hk=2, mask=CAUSAL, nc=None, nt=None, g=0, rab=False, S=None):
+    return wl.jagged_case(seed, lengths, Hq, Hk, 16, "fp8", mask_type=mask, num_context=nc, num_targets=nt,
+                          target_group_size=g, rab_std=0.5 if rab else None, max_seq_len=S, alpha=0.35,
+                          out_scale=0.3)
+
+
+def dense_fp8(c):
+    """Per sequence and head: out_scale * (M * E4M3(silu(alpha (Q K^T + R)))) V
+    with BLAS matmul, scipy's logistic function and torch's E4M3 cast; the
+    mask comes from the rule-based sets."""
+    q, k, v = f64(c.q), f64(c.k), f64(c.v)
+    rab = None if c.rab is None else f64(c.rab)
+    Hq, Hk = q.shape[1], k.shape[1]
+    out = np.zeros_like(q)
+    for b in range(c.batch):
+        s0, s1 = c.seq_offsets[b], c.seq_offsets[b + 1]
+        L = s1 - s0
+        nc = 0 if c.num_context is None else c.num_context[b]
+        nt = 0 if c.num_targets is None else c.num_targets[b]
+        M = mask_from_rules(L, nc, nt, c.target_group_size, c.mask_type)
+        for h in range(Hq):
+            hk = h * Hk // Hq
+            S = q[s0:s1, h, :] @ k[s0:s1, hk, :].T
+            if rab is not None:
+                S = S + np.where(M, rab[b, h, :L, :L], 0.0)
+            X = c.alpha * S
+            P = np.where(M, torch_e4m3(X * expit(X)), 0.0)
+            out[s0:s1, h, :] = c.out_scale * (P @ v[s0:s1, hk, :])
+    return out
+
+
+@pytest.mark.parametrize("kind", ["causal", "none", "ctx_tgt_g3", "gqa_rab"])
+def test_fp8_oracle_matches_dense_library(kind):
+    """The FP8 cast reading: E4M3 inputs, P cast to E4M3 before the product
+    with V, against the dense formulation with the library cast."""
+    if kind == "causal":
+        c = fp8_case(21, [13, 1, 20])
+    elif kind == "none":
+        c = fp8_case(22, [5, 17, 9], mask=NONE)
+    elif kind == "ctx_tgt_g3":
+        c = fp8_case(23, [19, 24, 7], nc=(0, 5), nt=(0, 9), g=3)
+    else:
+        c = fp8_case(24, [11, 16], Hq=6, Hk=2, nt=(0, 4), g=1, rab=True)
+    for t in (c.q, c.k, c.v):
+        assert t.dtype == E4M3
+    got = run_oracle(c, p_fp8=True)
+    np.testing.assert_allclose(got, dense_fp8(c), rtol=1e-12, atol=1e-13)
+    # the cast is real: without it the result moves by the E4M3 step of P
+    plain = run_oracle(c)
+    rel = np.linalg.norm(got - plain) / np.linalg.norm(plain)
+    assert 1e-3 < rel < 0.2, rel
+
+
+def test_fp8_constant_rab_unit_values_closed_form():
+    """Q = 0, rab = c, V = 1: every visible term is E4M3(silu(alpha c)), so
+    O[i, :] = out_scale * E4M3(silu(alpha c)) * (visible keys of row i)."""
+    L, D, alpha, out_scale, cst = 23, 16, 0.35, 0.3, 1.7
+    nc, nt, g = 3, 6, 2
+    rab = np.full((1, 1, L, L), cst)
+    out = oracle.hstu_fwd(np.zeros((L, 1, D)), np.zeros((L, 1, D)), np.ones((L, 1, D)), [0, L], rab=rab,
+                          num_context=[nc], num_targets=[nt], max_seq_len=L, target_group_size=g, alpha=alpha,
+                          out_scale=out_scale, p_fp8=True)
+    p8 = float(torch_e4m3([alpha * cst * expit(alpha * cst)])[0])
+    assert p8 != alpha * cst * expit(alpha * cst)
+    counts = closed_form_counts(L, nc, nt, g)
+    np.testing.assert_allclose(out[:, 0, :], out_scale * p8 * np.repeat(np.asarray(counts, float)[:, None], D, 1),
+                               rtol=1e-14)
