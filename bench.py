@@ -32,9 +32,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "fp8": 5000.0}  # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
-ELEM = {"bf16": 2, "f16": 2, "f32": 4}
+ELEM = {"bf16": 2, "f16": 2, "f32": 4, "fp8": 1}
+OUT_ELEM = {"fp8": 2}  # the FP8 cast writes bf16
 FLUSH_BYTES = 1 << 30  # written before each cold step: > 256 MB Infinity Cache + 8 x 4 MB L2
 
 # The roof that binds each workload's forward kernel (algorithmic flops and
@@ -43,7 +44,8 @@ FLUSH_BYTES = 1 << 30  # written before each cold step: > 256 MB Infinity Cache 
 # or a KV cache. The tiny fp32 workload is launch-bound; its line is
 # priced against the fp32 MFMA peak.
 BOUND = {"tiny_fp32_bidirectional": "mfma", "bf16_mha_causal": "mfma", "fp16_gqa_causal": "mfma",
-         "bf16_rab_target": "hbm", "bf16_paged_target": "hbm", "bf16_custom_mask": "hbm", "bf16_delta_qk": "hbm"}
+         "bf16_rab_target": "hbm", "bf16_paged_target": "hbm", "bf16_custom_mask": "hbm", "bf16_delta_qk": "hbm",
+         "fp8_gqa_causal": "mfma"}
 
 
 def parse():
@@ -281,7 +283,8 @@ def workload_work(name, c):
                 pairs = metrics.pairs_delta(c.key_lengths, c.lengths, c.num_context, c.num_targets,
                                             c.target_group_size, c.mask_type)
             alg_bytes = metrics.algorithmic_bytes_jagged(T, c.num_heads_q, c.num_heads_kv, c.head_dim, E,
-                                                         pairs if c.rab is not None else 0, Tk=Tk)
+                                                         pairs if c.rab is not None else 0, Tk=Tk,
+                                                         out_bytes=OUT_ELEM.get(c.dtype))
         desc = dict(batch=c.batch, total_tokens=T, max_seq_len=c.max_seq_len, lengths_min=int(c.lengths.min()),
                     lengths_max=int(c.lengths.max()))
         if c.seq_offsets_k is not None:
@@ -395,7 +398,7 @@ def oracle_sample(c, name, flops_full, stride):
     run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, mask=mask, seq_offsets_k=c.seq_offsets_k,
                                   num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
                                   mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                                  out_scale=c.out_scale, rows=rows)
+                                  out_scale=c.out_scale, rows=rows, p_fp8=c.dtype == "fp8")
     return run, fl, desc
 
 
@@ -415,7 +418,7 @@ def _time_for(run, seconds):
 # (one thread) of CPU time.
 ORACLE_STRIDES = {"tiny_fp32_bidirectional": (1, 1), "bf16_mha_causal": (1, 8), "bf16_rab_target": (16, 128),
                   "fp16_gqa_causal": (16, 128), "bf16_paged_target": (1, 8), "bf16_custom_mask": (1, 8),
-                  "bf16_delta_qk": (1, 8)}
+                  "bf16_delta_qk": (1, 8), "fp8_gqa_causal": (16, 128)}
 
 
 def cpu_baseline(c, name, flops_full):
@@ -534,7 +537,9 @@ def measure(name, args, dev):
            "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": dtype, "data": "synthetic (seeded numpy draws, rounded to dtype)",
-           "config": dict(workload=name, **desc), "pct_of_mfma_peak": round(100 * value / peak_f, 2),
+           "config": dict(workload=name, **desc),
+           # the metric's percentage: of the dense bf16 peak (of the fp32 peak for the fp32 workload)
+           "pct_of_mfma_peak": round(100 * value / (peak_f if dtype == "f32" else PEAK_TFLOPS["bf16"]), 2),
            "timing": "cold: a 1 GiB device write before each step (outside the events) evicts L2 and Infinity "
                      "Cache; per-step HIP events on the launch stream",
            "ms_per_step_median": round(statistics.median(step_ms), 5),
@@ -570,7 +575,8 @@ def main():
         copy_calibration(dev)
         return
     names = ["tiny_fp32_bidirectional", "bf16_mha_causal", "bf16_rab_target", "fp16_gqa_causal",
-             "bf16_paged_target", "bf16_custom_mask", "bf16_delta_qk"] if args.all else [args.workload]
+             "bf16_paged_target", "bf16_custom_mask", "bf16_delta_qk", "fp8_gqa_causal"] if args.all \
+        else [args.workload]
     for name in names:
         print(f"[bench] {name}: building inputs", file=sys.stderr, flush=True)
         res = measure(name, args, dev)

@@ -36,7 +36,10 @@ HSTU_ERR_UNSUPPORTED = 2
 HSTU_ERR_WORKSPACE = 3
 HSTU_ERR_HIP = 4
 
-DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float8_e4m3fn: 3}
+# The FP8 cast (q, k, v in E4M3) writes bf16; rab and the user mask would be
+# bf16 too (the library rejects them with FP8 inputs).
+OUT_DTYPES = {torch.float8_e4m3fn: torch.bfloat16}
 
 # Every symbol include/hstu.h declares.
 EXPORTED = ("hstu_fwd_workspace_size", "hstu_fwd", "hstu_fwd_plan", "hstu_fwd_run", "hstu_fwd_paged_workspace_size",
@@ -210,10 +213,11 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
     if out_scale is None:
         out_scale = 1.0 / max_seq_len
     heads = {}
+    side = OUT_DTYPES.get(dtype, dtype)
     for name, t in (("rab", rab), ("mask", mask)):
         heads[name] = 1
         if t is not None:
-            _dev_tensor(t, name, dtype, device)
+            _dev_tensor(t, name, side, device)
             if t.dim() != 4 or t.shape[0] != B or t.shape[1] not in (1, q.shape[1]) or \
                     tuple(t.shape[2:]) != (max_seq_len, max_seq_len):
                 raise ValueError(f"{name} must be [{B}, {q.shape[1]} or 1, {max_seq_len}, {max_seq_len}], "
@@ -222,9 +226,9 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
     nc = _int32(num_context, "num_context", device)
     nt = _int32(num_targets, "num_targets", device)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(tuple(q.shape), dtype=side, device=device)
     else:
-        _dev_tensor(out, "out", dtype, device)
+        _dev_tensor(out, "out", side, device)
     Hq, Hk, D = int(q.shape[1]), int(k.shape[1]), int(q.shape[2])
     code = DTYPE_CODES[dtype]
     need = int(lib.hstu_fwd_workspace_size(B, max_seq_len, Hq, Hk, D, code, 0 if offk is None else 1))

@@ -20,17 +20,23 @@ constexpr int32_t kMaxBatch = 2048;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-bool dtype_ok(hstu_dtype_t dt) { return dt == HSTU_F32 || dt == HSTU_F16 || dt == HSTU_BF16; }
+bool dtype_ok(hstu_dtype_t dt) { return dt == HSTU_F32 || dt == HSTU_F16 || dt == HSTU_BF16 || dt == HSTU_FP8_E4M3; }
 
 bool head_dim_ok(int32_t d, hstu_dtype_t dt) {
   if (dt == HSTU_F32) return d == 32 || d == 64 || d == 128;
+  if (dt == HSTU_FP8_E4M3) return d == 128;
   return d == 32 || d == 64 || d == 128 || d == 256;
 }
 
 bool page_size_ok(int32_t ps) { return ps == 32 || ps == 64 || ps == 128 || ps == 256; }
 
 hstu::DType to_internal(hstu_dtype_t dt) {
-  return dt == HSTU_F32 ? hstu::DType::F32 : dt == HSTU_F16 ? hstu::DType::F16 : hstu::DType::BF16;
+  switch (dt) {
+    case HSTU_F32: return hstu::DType::F32;
+    case HSTU_F16: return hstu::DType::F16;
+    case HSTU_FP8_E4M3: return hstu::DType::FP8;
+    default: return hstu::DType::BF16;
+  }
 }
 
 // Checks shared by both entry points. Returns HSTU_OK or the error.
@@ -102,6 +108,9 @@ hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, con
   if (st != HSTU_OK) return st;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return HSTU_OK;
   if (mask_type == HSTU_MASK_CUSTOM && dtype == HSTU_F32) return HSTU_ERR_UNSUPPORTED;
+  // The FP8 cast is built for jagged calls with equal Q and K lengths,
+  // without rab or the user mask.
+  if (dtype == HSTU_FP8_E4M3 && (mask_type == HSTU_MASK_CUSTOM || seq_offsets_k || rab)) return HSTU_ERR_UNSUPPORTED;
   if (!seq_offsets || !aligned4(seq_offsets) || (seq_offsets_k && !aligned4(seq_offsets_k)))
     return HSTU_ERR_INVALID_ARG;
   if (phase & kRun) {
@@ -164,6 +173,8 @@ hstu_status_t paged(int phase, const void* q, const void* k_new, const void* v_n
                                   target_group_size, dtype, num_context, num_targets);
   if (st != HSTU_OK) return st;
   if (mask_type == HSTU_MASK_CUSTOM) return HSTU_ERR_UNSUPPORTED;  // the user mask is built for jagged calls
+  if (dtype == HSTU_FP8_E4M3 && batch > 0 && num_heads_q > 0 && head_dim > 0)
+    return HSTU_ERR_UNSUPPORTED;  // the FP8 cast is built for jagged calls
   if (page_size < 0) return HSTU_ERR_INVALID_ARG;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return HSTU_OK;
   if (!page_size_ok(page_size)) return HSTU_ERR_UNSUPPORTED;

@@ -8,7 +8,8 @@
 
 namespace hstu {
 
-enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+// FP8: q, k, v in OCP E4M3 (FN), out in bf16.
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
 
 // Everything one forward launch needs. Pointers are device memory.
 struct FwdArgs {

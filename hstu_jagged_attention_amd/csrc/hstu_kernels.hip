@@ -1197,6 +1197,305 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ------------------------------------------------------------------------
+// FP8 forward (the feature table's FP8 quantization row, "cast": element
+// quantization with no scale). Q, K and V are OCP E4M3 (FN) bytes; both
+// products run on v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands and fp32
+// accumulation; P = silu(alpha S) is cast to E4M3 in between (nearest, ties
+// to even, saturating at 448: the convert rounds to nearest even but turns
+// values past the format into NaN, so P is first clamped to 448); O is
+// stored in bf16. head_dim 128, no rab or user mask, jagged calls with equal
+// Q and K lengths.
+//
+// Layouts (checked on the device): the f8f6f4 MFMA maps the 32 bytes of a
+// lane to k in the same way for A and B, so a product only needs A and B
+// filled with the same key / feature order; its output layout is that of
+// the 16-bit kernel's 32x32 MFMA (lane = query, 16 keys or features per
+// lane). ds_read_b64_tr_b8 works on 16-lane groups: lane t of a group
+// receives byte t % 8 of the 8-byte reads of lanes 2i + t / 8, i = 0..7.
+//
+// K and V tiles are 64 rows of 128 bytes in LDS, with no padding; the
+// 16-byte chunk c of key row k sits at chunk slot c ^ swz(k) (the DMA loads
+// the chunk its slot needs, so the swizzle costs nothing). K uses
+// (k >> 1) & 7: the 16 rows of a 16-lane K-fragment read fill all 64 banks.
+// V uses ((k >> 3) & 3) << 1 with P's key order below: the 8 rows x 2
+// chunks a 32-lane half of a transposing V read touches fill all 64 banks.
+//
+// O^T += V^T P^T: lane (query n, half h) of the B operand holds, at byte
+// 8 q + i (q, i = 0..7), P for key 32 (q/2) + 8 (i/2) + 4 h + 2 (q%2) + i%2
+// -- which is element 4 (i/2) + 2 (q%2) + i%2 of S^T block q/2 in the same
+// lane -- and the A operand's transposing reads bring V rows in that order.
+// ------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline f32x16_t mfma_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ inline i32x2_t lds_read_tr8(const void* addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)addr);
+#else
+  return i32x2_t{};
+#endif
+}
+
+__device__ inline int swz_k8(int k) { return (k >> 1) & 7; }
+__device__ inline int swz_v8(int k) { return ((k >> 3) & 3) << 1; }
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_fp8_kernel(KParams p) {
+  using TO = __bf16;
+  constexpr int D = 128, BN = 64, ROW = D;  // bytes per E4M3 row
+  constexpr int TILE_B = BN * ROW;          // 8 KB per K or V tile
+  constexpr int NBLK = TILE_B / 1024;       // 1 KB DMA blocks per tile
+  constexpr int BLK_W = NBLK / kWaves;      // per wave
+  constexpr int NDB = D / 32;               // 32-feature blocks of O^T
+  constexpr int KS = D / 64;                // k steps of S^T
+  constexpr int NJB = BN / 32;              // 32-key blocks per tile
+  constexpr int OUT_ROW_B = D * 2;          // bf16 output row
+  static_assert(NBLK % kWaves == 0, "DMA blocks per wave");
+
+  __shared__ __attribute__((aligned(1024))) char smem_k0[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_v0[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_k1[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_v1[TILE_B];
+  __shared__ int sh_item[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const bool direct = p.direct_items > 0;
+  const int n_work = direct ? p.direct_items : *p.n_items * p.n_hg;
+  const int hpw = 1 << p.hpw_log2;
+  const uint32_t row_stride_b = (uint32_t)p.Hk * ROW;
+
+  // DMA geometry of this lane: block blk = wave + kWaves u, 16-byte slot
+  // blk * 64 + lane = key row slot / 8 of the tile, chunk slot slot % 8,
+  // which receives chunk (slot % 8) ^ swz(row) of that row.
+  uint32_t dma_k_off[BLK_W], dma_v_off[BLK_W];
+#pragma unroll
+  for (int u = 0; u < BLK_W; ++u) {
+    const int sl = (wave + kWaves * u) * 64 + lane, row = sl >> 3, pos = sl & 7;
+    dma_k_off[u] = (uint32_t)row * row_stride_b + 16u * (uint32_t)(pos ^ swz_k8(row));
+    dma_v_off[u] = (uint32_t)row * row_stride_b + 16u * (uint32_t)(pos ^ swz_v8(row));
+  }
+  // Transposing V reads: lane t16 = lane % 16 of its 16-lane group G reads,
+  // for read q, key row key8(q) at bytes 8 cs of chunk 2 db + (G & 1).
+  const int G = lane >> 4, t16 = lane & 15, ki = t16 >> 1, cs = t16 & 1;
+  auto key8 = [&](int q) { return 32 * (q >> 1) + 8 * (ki >> 1) + 4 * half + 2 * (q & 1) + (ki & 1); };
+
+  const bool dyn = (int)gridDim.x < n_work;
+  int w = blockIdx.x, parity = 0;
+  while (w < n_work) {
+    int w_next = n_work;
+    if (dyn && tid == 0) w_next = (int)gridDim.x + atomicAdd(p.counter, 1);
+    const int item = w / p.n_hg;
+    const int hg = w - item * p.n_hg;
+    int b, qt;
+    if (direct) {
+      qt = p.n_qt_max - 1 - item / p.batch;
+      b = item - (p.n_qt_max - 1 - qt) * p.batch;
+    } else {
+      const int packed = p.items[2 * item];
+      b = packed >> 16;
+      qt = packed & 0xffff;
+    }
+    const Seq s = load_seq<false>(p, b, CAUSAL);
+    if (direct && qt * p.bm >= s.Lq) break;
+    const int h = hg * hpw + (wave & (hpw - 1));
+    const int rb = wave >> p.hpw_log2;
+    const int hk = (hg * hpw) / p.group;
+    const int q_lo = qt * p.bm;
+    const int q_hi = min(q_lo + p.bm, s.Lq);
+    const int i_lo = s.Lh + q_lo, i_hi = s.Lh + q_hi - 1;
+    const int q_loc = q_lo + rb * kRowsPerWave + l32;
+    const bool row_ok = q_loc < s.Lq;
+    const bool wave_active = q_lo + rb * kRowsPerWave < s.Lq;
+    const int i = s.Lh + q_loc;
+
+    // K and V tile kt into LDS; rows past the sequence repeat its last row
+    // (finite, and P is zero there).
+    auto dma_tile = [&](int kt, char* kbuf, char* vbuf) {
+      const int j0 = kt * BN;
+      if (j0 + BN <= s.L) {
+        const char* kb = (const char*)p.k + ((size_t)(s.k_tok0 + j0) * p.Hk + hk) * ROW;
+        const char* vb = (const char*)p.v + ((size_t)(s.k_tok0 + j0) * p.Hk + hk) * ROW;
+#pragma unroll
+        for (int u = 0; u < BLK_W; ++u) {
+          const int blk = wave + kWaves * u;
+          dma16(kb + dma_k_off[u], kbuf + blk * 1024);
+          dma16(vb + dma_v_off[u], vbuf + blk * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < BLK_W; ++u) {
+          const int blk = wave + kWaves * u;
+          const int sl = blk * 64 + lane, row = sl >> 3, pos = sl & 7;
+          const int j = min(j0 + row, s.L - 1);
+          const char* base = (const char*)p.k + ((size_t)(s.k_tok0 + j) * p.Hk + hk) * ROW;
+          const char* vbase = (const char*)p.v + ((size_t)(s.k_tok0 + j) * p.Hk + hk) * ROW;
+          dma16(base + 16 * (pos ^ swz_k8(row)), kbuf + blk * 1024);
+          dma16(vbase + 16 * (pos ^ swz_v8(row)), vbuf + blk * 1024);
+        }
+      }
+    };
+
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
+    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
+    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    if (n_tiles > 0) dma_tile(tile_at(0), smem_k0, smem_v0);
+
+    // Q fragments (B operand of S^T = K Q^T): lane (query l32, half) holds
+    // features 64 ks + 32 half .. + 31 of its row, as K's A operand does.
+    i32x8_t qf[KS];
+    {
+      const char* qrow = (const char*)p.q + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * ROW + 32 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+        if (row_ok) {
+          x0 = *(const u32x4_t*)(qrow + 64 * ks);
+          x1 = *(const u32x4_t*)(qrow + 64 * ks + 16);
+        }
+        qf[ks] = i32x8_t{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+    }
+    const int hi_i = (i < s.nc) ? max(i, s.nc - 1) : i;
+    const int tlo_i = (p.g <= 0) ? s.H : (i >= s.H ? s.H + ((i - s.H) / p.g) * p.g : INT_MAX);
+    const int a_i = CAUSAL ? min(hi_i, s.H - 1) : s.L - 1;
+    const int b_i = CAUSAL ? max(tlo_i, s.H) : INT_MAX;
+
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+    auto step = [&](int n, auto bufc) {
+      constexpr int BUF = decltype(bufc)::value;
+      const bool has_tile = n < n_tiles;
+      const int kt = tile_at(has_tile ? n : 0);
+      wait_vmem_all();
+      __syncthreads();
+      if (n + 1 < n_tiles) {
+        if constexpr (BUF == 0) dma_tile(tile_at(n + 1), smem_k1, smem_v1); else dma_tile(tile_at(n + 1), smem_k0, smem_v0);
+      }
+      if (!wave_active || !has_tile) return;
+      const char* kbuf = BUF == 0 ? smem_k0 : smem_k1;
+      const char* vbuf = BUF == 0 ? smem_v0 : smem_v1;
+      const int j0 = kt * BN;
+      const int j1 = min(j0 + BN, s.L);
+      const bool full = (j0 + BN <= s.L) &&
+                        (!CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc)));
+
+      // S^T = K Q^T: lane (key row, half) reads features 64 ks + 32 half .. + 31.
+      f32x16_t sacc[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int row = jb * 32 + l32;
+        const char* rbase = kbuf + row * ROW;
+        const int sw = swz_k8(row);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c0 = 4 * ks + 2 * half;
+          const u32x4_t a0 = *(const u32x4_t*)(rbase + 16 * (c0 ^ sw));
+          const u32x4_t a1 = *(const u32x4_t*)(rbase + 16 * ((c0 + 1) ^ sw));
+          const i32x8_t kf = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          const f32x16_t zero = {};
+          sacc[jb] = mfma_e4m3(kf, qf[ks], ks == 0 ? zero : sacc[jb]);
+        }
+      }
+
+      // Epilogue: P = min(silu(alpha s), 448), cast to E4M3, packed as the
+      // B operand of O^T (byte order in the comment above the kernel).
+      uint32_t vis[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const int jbase = j0 + jb * 32 + 4 * half;
+        const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
+        vis[jb] = full ? 0xffffffffu : (low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg)));
+      }
+      auto pval = [&](int jb, int r) -> float {
+        float sv = sacc[jb][r];
+        // Masked keys get s = +0 (bitwise AND with the visibility bit), hence p = 0 exactly.
+        const int off = 8 * (r / 4) + (r % 4);
+        const int keep = (int)(vis[jb] << (31 - off)) >> 31;
+        sv = __builtin_bit_cast(float, __builtin_bit_cast(int, sv) & keep);
+        const float a = sv * p.alpha;
+        const float e = __builtin_amdgcn_exp2f(a * -kLog2e);
+        const float pv = a * __builtin_amdgcn_rcpf(1.f + e);
+        return __builtin_fminf(pv, 448.f);
+      };
+      // Word 2 q + w holds bytes 8 q + 4 w .. + 3, i.e. i2 = 2 w (low half) and
+      // i2 = 2 w + 1 (high half) of the pairs (i, i + 1) = (2 i2, 2 i2 + 1).
+      i32x8_t pb = {};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int wh = 0; wh < 2; ++wh) {
+          const int jb = q >> 1, r_lo = 4 * (2 * wh) + 2 * (q & 1), r_hi = 4 * (2 * wh + 1) + 2 * (q & 1);
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(pval(jb, r_lo), pval(jb, r_lo + 1), 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(pval(jb, r_hi), pval(jb, r_hi + 1), word, true);
+          pb[2 * q + wh] = word;
+        }
+
+      // O^T += V^T P^T: four transposing reads per 32-feature block.
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        i32x2_t part[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = key8(q);
+          part[q] = lds_read_tr8(vbuf + row * ROW + 16 * ((2 * db + (G & 1)) ^ swz_v8(row)) + 8 * cs);
+        }
+        const i32x8_t vf = {part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+        o[db] = mfma_e4m3(vf, pb, o[db]);
+      }
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      step(t, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    // Output: stage the wave's 32 x D bf16 rows through LDS (its own 8 KB
+    // buffer) and store whole rows, 16 bytes per lane.
+    __syncthreads();
+    {
+      char* stg = wave == 0 ? smem_k0 : wave == 1 ? smem_v0 : wave == 2 ? smem_k1 : smem_v1;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int r32 = ln & 31, hf = ln >> 5;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          TO y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (TO)(o[db][4 * a + e] * p.out_mul);
+          const int f0 = db * 32 + 8 * a + 4 * hf;
+          *(u32x2_t*)(stg + r32 * OUT_ROW_B + (((f0 >> 3) ^ swz<D>(r32)) * 16) + (f0 & 7) * 2) = *(const u32x2_t*)y;
+        }
+      __builtin_amdgcn_wave_barrier();
+      constexpr int CPR = D / 8;
+      const int row0 = q_lo + rb * kRowsPerWave;
+#pragma unroll
+      for (int it = 0; it < kRowsPerWave * CPR / 64; ++it) {
+        const int idx = it * 64 + ln, row = idx / CPR, c = idx % CPR;
+        const u32x4_t x = *(const u32x4_t*)(stg + row * OUT_ROW_B + ((c ^ swz<D>(row)) * 16));
+        if (wave_active && row0 + row < s.Lq)
+          *(u32x4_t*)((TO*)p.out + ((size_t)(s.q_tok0 + row0 + row) * p.Hq + h) * D + c * 8) = x;
+      }
+    }
+    if (tid == 0) sh_item[parity] = w_next;
+    __syncthreads();
+    w = __builtin_amdgcn_readfirstlane(sh_item[parity]);
+    parity ^= 1;
+  }
+  if (dyn) leave_queue(p);
+}
+
+// ------------------------------------------------------------------------
 // Split-K reduction: for each split item and head group, O = out_mul *
 // (partial of chunk 0 + chunk 1 + ...), summed in chunk order so the result
 // does not depend on which workgroup finished first.
@@ -1480,6 +1779,13 @@ KernelFn pick32(bool causal, bool rab) {
 template <bool PAGED>
 KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, bool user_mask, bool delta, int* wgs_per_cu,
               int* threads) {
+  if (dt == DType::FP8) {
+    // FP8 cast: head_dim 128 jagged calls without rab, user mask or key offsets.
+    if (PAGED || D != 128 || rab || user_mask || delta) return nullptr;
+    *wgs_per_cu = 2;
+    *threads = kThreads;
+    return causal ? fwd_fp8_kernel<true> : fwd_fp8_kernel<false>;
+  }
   ksplit = ksplit && !PAGED && dt != DType::F32 && D <= 128 && !user_mask;
   if (user_mask && (PAGED || dt == DType::F32)) return nullptr;
   *wgs_per_cu = ksplit ? 1 : ((dt == DType::F32 || D >= 256) ? 1 : 2);
@@ -1554,7 +1860,7 @@ constexpr int kSplitUnits = 1024;  // (slot, head group) pairs of partial sums
 // sequence, the fixed cost of each extra chunk (queue pop, sequence and Q
 // loads, partial sums, the reduction launch) outweighed the shorter critical
 // path on the measured workloads, so they are not split.
-bool use_split(bool split_keys, DType dtype) { return split_keys && dtype != DType::F32; }
+bool use_split(bool split_keys, DType dtype) { return split_keys && dtype != DType::F32 && dtype != DType::FP8; }
 
 // cap > 0: a workspace of at most cap bytes (the static scratch of the
 // allocation-free entry point). Split items then get as many partial-sum
@@ -1658,7 +1964,10 @@ KParams make_params(const FwdArgs& a) {
     p.y_mul = std::ldexp(1.f, k);
     p.c_q = std::ldexp(p.c_exp, -k);
   }
-  p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : -a.out_scale / kLog2e;
+  // The fp32 kernel folds alpha into the output scale and the 16-bit kernels
+  // -1/log2(e) (see the kernels); the FP8 kernel computes P itself.
+  p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : a.dtype == DType::FP8 ? a.out_scale
+                                                                                     : -a.out_scale / kLog2e;
   const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256;
   // One chunk per two resident workgroups: measured against 4x, 2x, 1/2x and
   // 1/4x that on the paged and delta-QK workloads (fewer chunks lengthen the

@@ -100,12 +100,15 @@ def effective_flops(pairs_one_head: int, num_heads_q: int, head_dim: int) -> flo
 
 
 def algorithmic_bytes_jagged(T: int, num_heads_q: int, num_heads_kv: int, head_dim: int, elem_bytes: int,
-                             rab_pairs_one_head: int = 0, Tk: Optional[int] = None, extra_bytes: float = 0.0) -> float:
+                             rab_pairs_one_head: int = 0, Tk: Optional[int] = None, extra_bytes: float = 0.0,
+                             out_bytes: Optional[int] = None) -> float:
     """Compulsory HBM bytes: Q and O once (T query rows), K and V once (Tk
     key rows, default T), rab only for the visible pairs (the method never
     reads masked rab), plus extra_bytes (a user mask, whose every entry
-    inside the sequences is read once per mask head)."""
-    qo = 2.0 * T * num_heads_q * head_dim * elem_bytes
+    inside the sequences is read once per mask head). out_bytes: bytes per
+    output element when they differ from the inputs' (the FP8 cast writes
+    bf16)."""
+    qo = T * num_heads_q * head_dim * (elem_bytes + (elem_bytes if out_bytes is None else out_bytes))
     kv = 2.0 * (T if Tk is None else Tk) * num_heads_kv * head_dim * elem_bytes
     rab = float(rab_pairs_one_head) * num_heads_q * elem_bytes
     return qo + kv + rab + extra_bytes

@@ -67,14 +67,22 @@ typedef enum {
   HSTU_ERR_HIP = 4          /* a HIP launch failed; the HIP error is left for hipGetLastError */
 } hstu_status_t;
 
-typedef enum { HSTU_F32 = 0, HSTU_F16 = 1, HSTU_BF16 = 2 } hstu_dtype_t;
+/* HSTU_FP8_E4M3 is the FP8 cast (the feature table's FP8 quantization row,
+ * "cast": element-level quantization with no scale): q, k and v are OCP
+ * E4M3 (FN) bytes (1 byte per element: sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, largest finite value 448, no infinities); both products
+ * run on E4M3 operands with fp32 accumulation; P = silu(alpha * S) is cast
+ * to E4M3 (nearest, ties to even, saturating at +-448) before the product
+ * with V; out is bf16. Supported for jagged calls with head_dim 128,
+ * without rab, the user mask or seq_offsets_k. */
+typedef enum { HSTU_F32 = 0, HSTU_F16 = 1, HSTU_BF16 = 2, HSTU_FP8_E4M3 = 3 } hstu_dtype_t;
 
 typedef enum { HSTU_MASK_CAUSAL = 0, HSTU_MASK_NONE = 2, HSTU_MASK_CUSTOM = 3 } hstu_mask_t;
 
 /* Supported sizes: batch in [0, 2048] (the page's B range; larger batches
  * return HSTU_ERR_INVALID_ARG and a workspace size of 0); head_dim in
- * {32, 64, 128, 256} for f16/bf16 and {32, 64, 128} for f32 (the page
- * allows multiples of 16 up to 512); num_heads_q % num_heads_kv == 0 (the
+ * {32, 64, 128, 256} for f16/bf16, {32, 64, 128} for f32 and 128 for
+ * FP8 (the page allows multiples of 16 up to 512); num_heads_q % num_heads_kv == 0 (the
  * page's GQA rule); page_size in {32, 64, 128, 256}; max_seq_len in
  * [1, 20480]; rab and user-mask head counts 1 or num_heads_q; the user mask
  * (HSTU_MASK_CUSTOM) in f16/bf16 jagged calls. */
@@ -106,7 +114,8 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
  *  mask          [batch, mask_num_heads, max_seq_len, max_seq_len] dtype with
  *                HSTU_MASK_CUSTOM, else NULL. mask_num_heads is num_heads_q or
  *                1; indexed as rab. f16/bf16 only.
- *  out           [Tq, num_heads_q, head_dim]   dtype (written for every query)
+ *  out           [Tq, num_heads_q, head_dim]   dtype, bf16 for HSTU_FP8_E4M3
+ *                (written for every query)
  *  seq_offsets   [batch + 1] int32, non-decreasing, seq_offsets[0] == 0.
  *  seq_offsets_k [batch + 1] int32, or NULL (keys = queries). When given, the
  *                Lq = seq_offsets[b+1] - seq_offsets[b] queries of sequence b
@@ -126,8 +135,9 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
  * without HSTU_MASK_CUSTOM or HSTU_MASK_CUSTOM without a mask, rab or mask
  * head counts other than 1 and num_heads_q, target_group_size < 0 or an
  * unknown mask code; HSTU_ERR_UNSUPPORTED for mask code 1, head_dim, dtype,
- * or HSTU_MASK_CUSTOM in f32; HSTU_ERR_WORKSPACE if workspace_bytes is too
- * small; HSTU_ERR_HIP if a launch fails.
+ * HSTU_MASK_CUSTOM in f32, or HSTU_FP8_E4M3 with rab, the user mask or
+ * seq_offsets_k; HSTU_ERR_WORKSPACE if workspace_bytes is too small;
+ * HSTU_ERR_HIP if a launch fails.
  */
 hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
                        const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
@@ -192,7 +202,7 @@ size_t hstu_fwd_paged_workspace_size(int32_t batch, int32_t page_size, int32_t m
  * sequence of history_len + Tq_b tokens; the mask (num_context, num_targets,
  * target_group_size) is applied on those absolute positions. No rab and no
  * user mask. Errors as hstu_fwd, plus HSTU_ERR_UNSUPPORTED for page_size
- * outside {32, 64, 128, 256} and for HSTU_MASK_CUSTOM.
+ * outside {32, 64, 128, 256}, for HSTU_MASK_CUSTOM and for HSTU_FP8_E4M3.
  */
 hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new, void* out,
                              const int32_t* seq_offsets_q, const void* kv_cache, const int32_t* page_offsets,

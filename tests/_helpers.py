@@ -15,6 +15,10 @@ TOL = {
     "f32": dict(max_abs=1e-4, rel_l2=1e-5, rel_max=1e-3),
     "f16": dict(max_abs=2e-2, rel_l2=1e-2, rel_max=2e-2),
     "bf16": dict(max_abs=2e-2, rel_l2=1e-2, rel_max=2e-2),
+    # The FP8 cast writes bf16 and the oracle models its E4M3 cast of P, so
+    # the bf16 bars apply (the cast itself moves O by about 2 % rel-L2, see
+    # the FP8 parity test).
+    "fp8": dict(max_abs=2e-2, rel_l2=1e-2, rel_max=2e-2),
 }
 
 
@@ -56,7 +60,7 @@ def oracle_jagged(c, rows=None) -> np.ndarray:
                            mask=None if c.mask is None else f64(c.mask), seq_offsets_k=c.seq_offsets_k,
                            num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
                            mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                           out_scale=c.out_scale, rows=rows)
+                           out_scale=c.out_scale, rows=rows, p_fp8=c.dtype == "fp8")
 
 
 def oracle_jagged_sampled(c, picks):
@@ -77,7 +81,7 @@ def oracle_jagged_sampled(c, picks):
                                num_targets=None if c.num_targets is None else c.num_targets[b:b + 1],
                                max_seq_len=c.max_seq_len, mask_type=c.mask_type,
                                target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale,
-                               rows=rows)
+                               rows=rows, p_fp8=c.dtype == "fp8")
         res[b] = (np.array([s0 + r for r, _ in rows]), np.array([h for _, h in rows]), vals)
     return res
 

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hstu.h")
 
 OK, INVAL, UNSUP, WS = hj.HSTU_OK, hj.HSTU_ERR_INVALID_ARG, hj.HSTU_ERR_UNSUPPORTED, hj.HSTU_ERR_WORKSPACE
-BF16, F16, F32 = 2, 1, 0
+BF16, F16, F32, FP8 = 2, 1, 0, 3
 FAKE = 0x10000  # 16-byte aligned host integer, never dereferenced (calls fail validation first)
 
 
@@ -106,6 +106,11 @@ def test_empty_inputs_are_a_noop(lib):
     (dict(mask=2, nc=FAKE), INVAL),
     (dict(ws=None), WS),
     (dict(wsb=16), WS),
+    (dict(dt=FP8, D=64), UNSUP),              # the FP8 cast is built for head_dim 128
+    (dict(dt=FP8, rab=FAKE), UNSUP),          # ... without rab
+    (dict(dt=FP8, mask=3, umask=FAKE), UNSUP),  # ... or the user mask
+    (dict(dt=FP8, offk=FAKE), UNSUP),         # ... or separate key offsets
+    (dict(dt=4), UNSUP),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -122,6 +127,7 @@ def test_fwd_rejects(lib, kw, code):
     (dict(mask=3), UNSUP),
     (dict(wsb=8), WS),
     (dict(B=2049), INVAL),
+    (dict(dt=FP8), UNSUP),                    # the FP8 cast is built for jagged calls
 ])
 def test_paged_rejects(lib, kw, code):
     assert paged(lib, **kw) == code

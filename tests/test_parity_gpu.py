@@ -246,6 +246,52 @@ def test_fp16_large_q_alpha_one(dev, batch):
     assert_parity(got, oracle_jagged(c), "f16", "large q")
 
 
+# ------------------------------------------------------------ FP8 cast (E4M3 inputs, P cast to E4M3, bf16 out)
+FP8_CASES = [
+    # (name, lengths, Hq, Hk, mask, nc, nt, g)
+    ("fp8_direct_causal", [200, 77, 300, 1], 4, 4, CAUSAL, None, None, 0),
+    ("fp8_direct_gqa_ctx_targets", [150, 270, 33], 8, 2, CAUSAL, (0, 20), (1, 40), 1),
+    ("fp8_direct_bidirectional", [65, 129, 200], 2, 1, NONE, None, None, 0),
+    ("fp8_work_list_targets_g3", [int(x) for x in np.resize([0, 1, 31, 33, 64, 65, 127, 129, 300, 257], 90)], 4, 2,
+     CAUSAL, (0, 12), (1, 50), 3),
+    ("fp8_work_list_mha", [int(x) for x in np.resize([63, 64, 65, 200, 255, 256, 511], 70)], 4, 4, CAUSAL, None,
+     (0, 30), 1),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[e[0] for e in FP8_CASES])
+def test_fp8_cast(dev, case):
+    """FP8 cast on v_mfma_f32_32x32x64_f8f6f4, element by element against the
+    oracle with its E4M3 cast of P; the oracle without that cast is much
+    further away, so the kernel does cast P."""
+    name, lengths, Hq, Hk, mask, nc, nt, g = case
+    c = wl.jagged_case(zlib.crc32(name.encode()) % (1 << 30), lengths, Hq, Hk, 128, "fp8", mask_type=mask,
+                       num_context=nc, num_targets=nt, target_group_size=g, name=name)
+    say(name, "batch", c.batch, "heads", Hq, Hk)
+    got = run_jagged(c, dev)
+    assert got.dtype == torch.bfloat16
+    _, rel_cast = assert_parity(got, oracle_jagged(c), "fp8", name)
+    import oracle as orc
+    plain = orc.hstu_fwd(f64(c.q), f64(c.k), f64(c.v), c.seq_offsets, num_context=c.num_context,
+                         num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
+                         target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
+    g64 = f64(got)
+    rel_plain = float(np.linalg.norm(g64 - plain) / np.linalg.norm(plain))
+    assert rel_plain > 3 * rel_cast, (rel_plain, rel_cast)
+
+
+def test_fp8_workload_reduced_and_sampled(dev):
+    c = wl.fp8_gqa_causal(batch=2)
+    say("fp8_gqa_causal batch 2", c.lengths.tolist())
+    assert_parity(run_jagged(c, dev), oracle_jagged(c), "fp8", "fp8_gqa_causal reduced")
+    c = wl.fp8_gqa_causal()
+    say("fp8_gqa_causal full size: B", c.batch, "T", int(c.seq_offsets[-1]))
+    got = run_jagged(c, dev).cpu()
+    ref = oracle_jagged_sampled(c, _picks(c))
+    for b, (toks, heads, vals) in ref.items():
+        assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, "fp8", f"fp8_gqa_causal seq {b}")
+
+
 def test_every_row_is_written(dev):
     c = wl.jagged_case(5, [45, 0, 200, 1], 4, 2, 128, "bf16", num_targets=(1, 9), target_group_size=1)
     say("every_row_is_written")
