@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include "hstu.h"
 #include "hstu_internal.h"
 
@@ -86,7 +88,33 @@ namespace {
 
 enum Phase { kPlan = 1, kRun = 2, kBoth = 3 };
 
+// HSTU_VALIDATE=1 in the environment (read at every call) turns on the
+// debug check of the device-side inputs: a validation kernel writes its
+// verdict into the workspace header, the call waits for the stream
+// and reads it, and returns HSTU_ERR_INVALID_ARG without launching the
+// forward kernels when the inputs break the rules. Off by default: the
+// library then never synchronises and never reads device memory.
+bool validate_mode() {
+  const char* v = std::getenv("HSTU_VALIDATE");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+hstu_status_t validate(const hstu::FwdArgs& a) {
+  // An unused word of the workspace header (its first 64-byte line holds
+  // only the plan's item count, in word 0).
+  int32_t* flag = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + 32);
+  if (hstu::launch_validate(a, flag) != hipSuccess) return HSTU_ERR_HIP;
+  int32_t host = 1;
+  if (hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, a.stream) != hipSuccess) return HSTU_ERR_HIP;
+  if (hipStreamSynchronize(a.stream) != hipSuccess) return HSTU_ERR_HIP;
+  return host == 0 ? HSTU_OK : HSTU_ERR_INVALID_ARG;
+}
+
 hstu_status_t enqueue(const hstu::FwdArgs& a, int phase) {
+  if (validate_mode()) {
+    const hstu_status_t st = validate(a);
+    if (st != HSTU_OK) return st;
+  }
   if ((phase & kPlan) && hstu::launch_plan(a) != hipSuccess) return HSTU_ERR_HIP;
   if ((phase & kRun) && hstu::launch_run(a) != hipSuccess) return HSTU_ERR_HIP;
   return HSTU_OK;

@@ -62,6 +62,11 @@ size_t fwd_workspace_bytes(int32_t batch, int32_t max_q_len, int32_t num_heads_q
 // with hipGetSymbolAddress), *bytes its size. Allocates nothing.
 hipError_t scratch_workspace(void** ptr, size_t* bytes);
 
+// Enqueues the validation kernel on args.stream: it writes 1 to *flag
+// (device memory) if the device-side offsets, lengths or page counters
+// break the rules the page leaves to the caller, else 0.
+hipError_t launch_validate(const FwdArgs& args, int32_t* flag);
+
 // Enqueues the planner on args.stream: it writes the work list into the
 // workspace and zeroes the work-queue counters.
 hipError_t launch_plan(const FwdArgs& args);

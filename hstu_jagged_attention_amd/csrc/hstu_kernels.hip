@@ -1705,6 +1705,50 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) v
 }
 
 // ------------------------------------------------------------------------
+// Validation of the device side inputs (debug mode): one workgroup checks
+// what the page leaves to the caller -- seq_offsets (and seq_offsets_k)
+// start at 0 and never decrease, every key sequence fits max_seq_len,
+// queries never outnumber their keys; paged calls: page_offsets start at 0
+// and never decrease, last_page_len is in [1, page_size] for requests that
+// own pages, and history + new tokens fit max_seq_len. It writes 1 to *flag
+// when anything fails, else 0.
+// ------------------------------------------------------------------------
+template <bool PAGED>
+__global__ __launch_bounds__(256) void validate_kernel(KParams p, int32_t* flag) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  int mine = 0;
+  if (threadIdx.x == 0) {
+    mine |= p.seq_offsets[0] != 0;
+    if (p.seq_offsets_k) mine |= p.seq_offsets_k[0] != 0;
+    if (PAGED) mine |= p.page_offsets[0] != 0;
+  }
+  for (int b = threadIdx.x; b < p.batch; b += blockDim.x) {
+    const int lq = p.seq_offsets[b + 1] - p.seq_offsets[b];
+    mine |= lq < 0;
+    int lk = lq;
+    if (p.seq_offsets_k) {
+      lk = p.seq_offsets_k[b + 1] - p.seq_offsets_k[b];
+      mine |= lk < 0 || lq > lk;
+    }
+    if (PAGED) {
+      const int np = p.page_offsets[b + 1] - p.page_offsets[b];
+      mine |= np < 0;
+      const int last = p.last_page_len[b];
+      if (np > 0) mine |= last < 1 || last > (1 << p.ps_log2);
+      const long long hist = np > 0 ? ((long long)(np - 1) << p.ps_log2) + last : 0;
+      mine |= hist + lq > p.max_seq_len;
+    } else {
+      mine |= lk > p.max_seq_len;
+    }
+  }
+  if (mine) atomicOr(&bad, 1);
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = bad;
+}
+
+// ------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------
 constexpr size_t kHeaderBytes = 256;
@@ -1992,6 +2036,15 @@ bool use_direct(const FwdArgs& a, const KParams& p) {
 }
 
 }  // namespace
+
+hipError_t launch_validate(const FwdArgs& a, int32_t* flag) {
+  const KParams p = make_params(a);
+  if (a.paged)
+    hipLaunchKernelGGL(validate_kernel<true>, dim3(1), dim3(256), 0, a.stream, p, flag);
+  else
+    hipLaunchKernelGGL(validate_kernel<false>, dim3(1), dim3(256), 0, a.stream, p, flag);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const FwdArgs& a) {
   const KParams p = make_params(a);

@@ -41,8 +41,14 @@
  *    initialisation and are scratch after the call. Calls that share one
  *    workspace must be ordered on one stream.
  *  - Validity of device arrays (offsets non-decreasing from 0, every length
- *    <= max_seq_len, page ids in range) is the caller's duty, as the page
- *    says for seq_offsets; it is not checked.
+ *    <= max_seq_len, queries never more than their keys, last_page_len in
+ *    [1, page_size], page ids in range) is the caller's duty, as the page
+ *    says for seq_offsets. With HSTU_VALIDATE=1 in the environment (a debug
+ *    mode, read at every call) each call first checks all of these but the
+ *    page ids on the device, waits for the stream, and returns
+ *    HSTU_ERR_INVALID_ARG without launching the forward kernels when one
+ *    fails. That mode synchronises, so it cannot be used under graph
+ *    capture; by default nothing is checked and nothing waits.
  *  - Return codes only; nothing is thrown across the ABI.
  *  - batch is at most 2048 (the page's B range).
  *  - If batch, num_heads_q or head_dim is 0 the input is empty: the call

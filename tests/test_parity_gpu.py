@@ -556,3 +556,125 @@ def test_random_configurations(dev, i):
         "S", c.max_seq_len)
     got = run_jagged(c, dev)
     assert_parity(got, oracle_jagged(c), c.dtype, c.name)
+
+
+# ------------------------------------------------------------ debug validation, guard bands, block-table permutation
+def _raw_fwd(c, dev, off, max_seq_len, offk=None, out=None):
+    """hstu_fwd through the C ABI with explicit int32 device offsets (no
+    marshalling checks on their contents); returns (status, out)."""
+    lib = hj.load_library()
+    import ctypes
+    q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+    out = torch.full(tuple(c.q.shape), 7.0, dtype=c.q.dtype, device=dev) if out is None else out
+    offd = torch.as_tensor(off, dtype=torch.int32, device=dev)
+    offkd = None if offk is None else torch.as_tensor(offk, dtype=torch.int32, device=dev)
+    B = len(off) - 1
+    Hq, Hk, D = c.num_heads_q, c.num_heads_kv, c.head_dim
+    code = hj.DTYPE_CODES[c.q.dtype]
+    need = int(lib.hstu_fwd_workspace_size(B, max_seq_len, Hq, Hk, D, code, 0 if offk is None else 1))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    P = ctypes.c_void_p
+    st = lib.hstu_fwd(P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), None, None, P(out.data_ptr()),
+                      P(offd.data_ptr()), None if offkd is None else P(offkd.data_ptr()), None, None, B, max_seq_len,
+                      Hq, Hk, D, 1, 1, CAUSAL, 0, c.alpha, c.out_scale, code, P(ws.data_ptr()), need,
+                      P(torch.cuda.current_stream(dev).cuda_stream))
+    torch.cuda.synchronize(dev)
+    return st, out
+
+
+@pytest.mark.parametrize("bad", ["first_not_zero", "decreasing", "too_long", "queries_exceed_keys"])
+def test_validate_mode_rejects_malformed_offsets(dev, bad, monkeypatch):
+    """HSTU_VALIDATE=1: malformed device offsets return HSTU_ERR_INVALID_ARG
+    and no forward kernel runs (out keeps its fill value); the same call with
+    valid offsets passes and matches the oracle."""
+    c = wl.jagged_case(321, [40, 70, 33], 4, 2, 64, "bf16")
+    good = [0, 40, 110, 143]
+    off, offk, S = list(good), None, c.max_seq_len
+    if bad == "first_not_zero":
+        off = [3, 40, 110, 143]
+    elif bad == "decreasing":
+        off = [0, 40, 30, 143]
+    elif bad == "too_long":
+        S = 60  # the second sequence has 70 keys
+    else:
+        offk = [0, 40, 100, 143]  # sequence 1: 70 queries, 60 keys
+    monkeypatch.setenv("HSTU_VALIDATE", "1")
+    say("validate", bad)
+    st, out = _raw_fwd(c, dev, off, S, offk=offk)
+    assert st == hj.HSTU_ERR_INVALID_ARG, st
+    assert bool((out == 7.0).all()), "a forward kernel ran on rejected inputs"
+    st, out = _raw_fwd(c, dev, good, c.max_seq_len)
+    assert st == hj.HSTU_OK
+    assert_parity(out, oracle_jagged(c), "bf16", "validated call")
+    monkeypatch.setenv("HSTU_VALIDATE", "0")
+    st, _ = _raw_fwd(c, dev, good, c.max_seq_len)
+    assert st == hj.HSTU_OK
+
+
+GUARD = 4096  # bytes of canary before and after each buffer
+
+
+def _guarded(nbytes, dev, fill):
+    buf = torch.full((GUARD + nbytes + GUARD,), fill, dtype=torch.uint8, device=dev)
+    return buf, buf[GUARD:GUARD + nbytes]
+
+
+@pytest.mark.parametrize("kind", ["direct", "work_list", "delta_split", "paged_split", "fp8"])
+def test_guard_bands_stay_intact(dev, kind):
+    """Canary bytes around out and around the workspace are untouched by valid
+    calls in every launch mode (direct, work list, key-split with the ordered
+    reduction, paged, FP8)."""
+    say("guard bands", kind)
+    if kind == "paged_split":
+        pc = wl.bf16_paged_target(batch=8)
+        need = hj.hstu_fwd_paged_workspace_size(pc.batch, pc.page_size, pc.max_seq_len, pc.num_heads_q,
+                                                pc.num_heads_kv, pc.head_dim, torch.bfloat16)
+        wbuf, ws = _guarded(need, dev, 0xA5)
+        obuf, ob = _guarded(pc.q.numel() * 2, dev, 0x5A)
+        out = ob.view(torch.bfloat16).view(tuple(pc.q.shape))
+        got = run_paged(pc, dev, out=out, workspace=ws)
+        ref = oracle_paged(pc)
+        assert_parity(got, ref, "bf16", "paged guarded")
+    else:
+        if kind == "direct":
+            c = wl.jagged_case(401, [150, 1, 67, 300], 8, 2, 128, "bf16", num_targets=(1, 20), target_group_size=1)
+        elif kind == "work_list":
+            c = wl.jagged_case(402, np.resize([0, 31, 65, 129, 300], 80), 4, 2, 64, "f16", num_targets=(1, 9),
+                               target_group_size=1, max_seq_len=300)
+        elif kind == "delta_split":
+            lk = [500 + 13 * i for i in range(48)]
+            lq = [1 + (5 * i) % 64 for i in range(48)]
+            c = wl.jagged_case(403, lk, 4, 4, 128, "bf16", num_targets=lq, target_group_size=1, q_lengths=lq)
+        else:
+            c = wl.jagged_case(404, np.resize([33, 200, 129], 60), 8, 2, 128, "fp8", num_targets=(1, 9),
+                               target_group_size=1)
+        odt = torch.bfloat16 if c.dtype == "fp8" else c.q.dtype
+        need = hj.hstu_fwd_workspace_size(c.batch, c.max_seq_len, c.num_heads_q, c.num_heads_kv, c.head_dim,
+                                          c.q.dtype, is_delta_qk=c.seq_offsets_k is not None)
+        wbuf, ws = _guarded(need, dev, 0xA5)
+        obuf, ob = _guarded(c.q.shape[0] * c.q.shape[1] * c.q.shape[2] * 2, dev, 0x5A)
+        out = ob.view(odt).view(tuple(c.q.shape))
+        got = run_jagged(c, dev, out=out, workspace=ws)
+        assert_parity(got, oracle_jagged(c), c.dtype, f"guarded {kind}")
+    torch.cuda.synchronize(dev)
+    for buf, fill, what in ((wbuf, 0xA5, "workspace"), (obuf, 0x5A, "out")):
+        head, tail = buf[:GUARD], buf[-GUARD:]
+        assert bool((head == fill).all()) and bool((tail == fill).all()), f"{what} guard band overwritten"
+
+
+def test_paged_block_table_permutation_bit_identical(dev):
+    """Moving the pages of the pool under a random permutation of their ids
+    (block table rewritten to match) leaves the paged output bit-identical."""
+    pc = wl.paged_case(55, [300, 64, 1000, 5, 0], [9, 3, 40, 1, 7], 4, 2, 128, "bf16", page_size=64,
+                       num_context=(0, 4), target_group_size=1, extra_pages=5)
+    say("block-table permutation")
+    a = run_paged(pc, dev)
+    rng = np.random.default_rng(9)
+    n_pool = pc.kv_cache.shape[0]
+    perm = rng.permutation(n_pool)  # new slot of old page p is perm[p]
+    kv2 = torch.empty_like(pc.kv_cache)
+    kv2[torch.as_tensor(perm)] = pc.kv_cache
+    pc.kv_cache = kv2
+    pc.page_ids = perm[pc.page_ids]
+    b = run_paged(pc, dev)
+    assert torch.equal(a, b)
