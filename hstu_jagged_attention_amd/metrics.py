@@ -11,6 +11,9 @@ header): with nt clamped to [0, L], H = L - nt and nc clamped to [0, H], a
 context row (i < nc) sees nc keys, a history row (nc <= i < H) sees i + 1,
 and a target row (i >= H) sees i + 1 when target_group_size g == 0 and
 H + ((i - H) mod g) + 1 otherwise. The bidirectional mask gives L per row.
+A local window W (the feature table's local-mask row, read as: key j is
+visible to query i only when i - j < W as well) keeps of those sets only the
+keys j >= i - W + 1.
 """
 from __future__ import annotations
 
@@ -22,8 +25,10 @@ MASK_CAUSAL = 0
 MASK_NONE = 2
 
 
-def visible_per_row(L: int, nc: int = 0, nt: int = 0, g: int = 0, mask_type: int = MASK_CAUSAL) -> np.ndarray:
-    """Number of visible keys for each query row 0..L-1 of one sequence."""
+def visible_per_row(L: int, nc: int = 0, nt: int = 0, g: int = 0, mask_type: int = MASK_CAUSAL,
+                    w: int = 0) -> np.ndarray:
+    """Number of visible keys for each query row 0..L-1 of one sequence
+    (w: the local window, 0 for none)."""
     L = int(L)
     if L <= 0:
         return np.zeros(0, dtype=np.int64)
@@ -33,16 +38,19 @@ def visible_per_row(L: int, nc: int = 0, nt: int = 0, g: int = 0, mask_type: int
     H = L - nt
     nc = min(max(int(nc), 0), H)
     i = np.arange(L, dtype=np.int64)
-    out = i + 1
-    out[:nc] = nc
+    lo = np.maximum(i - int(w) + 1, 0) if w > 0 else np.zeros(L, dtype=np.int64)  # first key in the window
+    out = i + 1 - lo
+    out[:nc] = nc - lo[:nc]
     if g > 0 and nt > 0:
         t = i[H:]
-        out[H:] = H + ((t - H) % g) + 1
+        gs = H + ((t - H) // g) * g  # first row of the target's group
+        out[H:] = np.maximum(H - lo[H:], 0) + t + 1 - np.maximum(gs, lo[H:])
     return out
 
 
 def pairs_jagged(seq_offsets: Sequence[int], num_context: Optional[Sequence[int]],
-                 num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int) -> int:
+                 num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int,
+                 local_window: int = 0) -> int:
     """Visible pairs summed over sequences, for ONE query head."""
     off = np.asarray(seq_offsets, dtype=np.int64)
     total = 0
@@ -50,30 +58,32 @@ def pairs_jagged(seq_offsets: Sequence[int], num_context: Optional[Sequence[int]
         L = int(off[b + 1] - off[b])
         nc = 0 if num_context is None else int(num_context[b])
         nt = 0 if num_targets is None else int(num_targets[b])
-        total += int(visible_per_row(L, nc, nt, target_group_size, mask_type).sum())
+        total += int(visible_per_row(L, nc, nt, target_group_size, mask_type, local_window).sum())
     return total
 
 
 def pairs_paged(history_lengths: Sequence[int], new_lengths: Sequence[int], num_context: Optional[Sequence[int]],
-                num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int) -> int:
+                num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int,
+                local_window: int = 0) -> int:
     """Visible pairs of the new-token rows only (the queries), ONE query head."""
     total = 0
     for b in range(len(history_lengths)):
         Lh, Lq = int(history_lengths[b]), int(new_lengths[b])
         nc = 0 if num_context is None else int(num_context[b])
         nt = 0 if num_targets is None else int(num_targets[b])
-        rows = visible_per_row(Lh + Lq, nc, nt, target_group_size, mask_type)
+        rows = visible_per_row(Lh + Lq, nc, nt, target_group_size, mask_type, local_window)
         total += int(rows[Lh:].sum())
     return total
 
 
 def pairs_delta(key_lengths: Sequence[int], query_lengths: Sequence[int], num_context: Optional[Sequence[int]],
-                num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int) -> int:
+                num_targets: Optional[Sequence[int]], target_group_size: int, mask_type: int,
+                local_window: int = 0) -> int:
     """Different Q and K lengths: the queries are the last Lq of Lk
     positions, so only those rows count (ONE query head)."""
     lk = np.asarray(key_lengths, dtype=np.int64)
     lq = np.asarray(query_lengths, dtype=np.int64)
-    return pairs_paged(lk - lq, lq, num_context, num_targets, target_group_size, mask_type)
+    return pairs_paged(lk - lq, lq, num_context, num_targets, target_group_size, mask_type, local_window)
 
 
 def user_mask_counts(mask: np.ndarray, lengths: Sequence[int], num_heads_q: int, rab_heads: int = 0):

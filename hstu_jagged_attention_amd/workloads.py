@@ -51,6 +51,7 @@ class JaggedCase:
     out_scale: float
     seq_offsets_k: Optional[np.ndarray] = None  # int64 [B+1], keys (None: same as queries)
     mask: Optional[torch.Tensor] = None  # [B, Hq or 1, S, S], mask_type 3 only
+    local_window: int = 0  # local mask window W (causal only; 0 = none)
 
     @property
     def batch(self) -> int:
@@ -99,6 +100,7 @@ class PagedCase:
     target_group_size: int
     alpha: float
     out_scale: float
+    local_window: int = 0
 
     @property
     def batch(self) -> int:
@@ -147,7 +149,7 @@ def jagged_case(seed: int, lengths: Sequence[int], num_heads_q: int, num_heads_k
                 rab_padding_nan: bool = True, max_seq_len: Optional[int] = None, alpha: Optional[float] = None,
                 out_scale: Optional[float] = None, name: str = "jagged", q_lengths: Optional[Sequence[int]] = None,
                 rab_heads: Optional[int] = None, mask_keep: Optional[float] = None,
-                mask_heads: Optional[int] = None) -> JaggedCase:
+                mask_heads: Optional[int] = None, local_window: int = 0) -> JaggedCase:
     """A jagged case with the given sequence lengths.
 
     Q, K, V ~ N(0, 1). rab ~ N(0, rab_std^2) when rab_std is given, with
@@ -202,14 +204,15 @@ def jagged_case(seed: int, lengths: Sequence[int], num_heads_q: int, num_heads_k
                       num_targets=nt, max_seq_len=S, mask_type=mask_type, target_group_size=target_group_size,
                       alpha=float(alpha if alpha is not None else 1.0 / math.sqrt(head_dim)),
                       out_scale=float(out_scale if out_scale is not None else 1.0 / S), seq_offsets_k=offsets_k,
-                      mask=mask)
+                      mask=mask, local_window=int(local_window))
 
 
 def paged_case(seed: int, history_lengths: Sequence[int], new_lengths: Sequence[int], num_heads_q: int,
                num_heads_kv: int, head_dim: int, dtype: str = "bf16", *, page_size: int = 64,
                mask_type: int = MASK_CAUSAL, num_context: IntSpec = None, num_targets: IntSpec = "new",
                target_group_size: int = 1, max_seq_len: Optional[int] = None, alpha: Optional[float] = None,
-               out_scale: Optional[float] = None, extra_pages: int = 0, name: str = "paged") -> PagedCase:
+               out_scale: Optional[float] = None, extra_pages: int = 0, name: str = "paged",
+               local_window: int = 0) -> PagedCase:
     """A paged case: request b has history_lengths[b] cached tokens in
     ceil(h / page_size) pages and new_lengths[b] new tokens (the queries).
 
@@ -248,7 +251,8 @@ def paged_case(seed: int, history_lengths: Sequence[int], new_lengths: Sequence[
                      num_context=nc, num_targets=nt, page_size=page_size, max_seq_len=S, mask_type=mask_type,
                      target_group_size=target_group_size,
                      alpha=float(alpha if alpha is not None else 1.0 / math.sqrt(head_dim)),
-                     out_scale=float(out_scale if out_scale is not None else 1.0 / S))
+                     out_scale=float(out_scale if out_scale is not None else 1.0 / S),
+                     local_window=int(local_window))
 
 
 # ---------------------------------------------------------------------------

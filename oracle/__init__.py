@@ -55,17 +55,17 @@ def _load():
     D = ctypes.c_double
     lib.hstu_oracle_silu.argtypes = [D]
     lib.hstu_oracle_silu.restype = D
-    lib.hstu_oracle_vis.argtypes = [I32, I64, I64, I64, I64, I64, I64]
+    lib.hstu_oracle_vis.argtypes = [I32, I64, I64, I64, I64, I64, I64, I64]
     lib.hstu_oracle_vis.restype = ctypes.c_int
-    lib.hstu_oracle_mask.argtypes = [I32, I64, I64, I64, I64, P]
+    lib.hstu_oracle_mask.argtypes = [I32, I64, I64, I64, I64, I64, P]
     lib.hstu_oracle_mask.restype = None
     lib.hstu_oracle_e4m3.argtypes = [D]
     lib.hstu_oracle_e4m3.restype = D
-    lib.hstu_oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I64, D, D,
-                                    I32, P, I64]
+    lib.hstu_oracle_fwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I64, I64, D,
+                                    D, I32, P, I64]
     lib.hstu_oracle_fwd.restype = ctypes.c_int
-    lib.hstu_oracle_fwd_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I64, D, D,
-                                          P, I64]
+    lib.hstu_oracle_fwd_paged.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I32, I64, I64, D,
+                                          D, P, I64]
     lib.hstu_oracle_fwd_paged.restype = ctypes.c_int
     lib.hstu_oracle_num_threads.argtypes = []
     lib.hstu_oracle_num_threads.restype = ctypes.c_int
@@ -107,28 +107,29 @@ def e4m3(x: float) -> float:
     return float(_load().hstu_oracle_e4m3(float(x)))
 
 
-def vis(mask_type: int, L: int, nc: int, nt: int, g: int, i: int, j: int) -> bool:
-    return bool(_load().hstu_oracle_vis(mask_type, L, nc, nt, g, i, j))
+def vis(mask_type: int, L: int, nc: int, nt: int, g: int, i: int, j: int, w: int = 0) -> bool:
+    return bool(_load().hstu_oracle_vis(mask_type, L, nc, nt, g, w, i, j))
 
 
-def mask_matrix(mask_type: int, L: int, nc: int = 0, nt: int = 0, g: int = 0) -> np.ndarray:
-    """The L x L visibility matrix of one sequence (bool)."""
+def mask_matrix(mask_type: int, L: int, nc: int = 0, nt: int = 0, g: int = 0, w: int = 0) -> np.ndarray:
+    """The L x L visibility matrix of one sequence (bool); w: local window."""
     out = np.zeros((L, L), dtype=np.uint8)
-    _load().hstu_oracle_mask(mask_type, L, nc, nt, g, _ptr(out))
+    _load().hstu_oracle_mask(mask_type, L, nc, nt, g, w, _ptr(out))
     return out.astype(bool)
 
 
 def hstu_fwd(q, k, v, seq_offsets, *, rab=None, mask=None, seq_offsets_k=None, num_context=None,
              num_targets=None, max_seq_len: int, mask_type: int = MASK_CAUSAL, target_group_size: int = 0,
              alpha: float = 1.0, out_scale: Optional[float] = None, rows: Optional[Sequence] = None,
-             p_fp8: bool = False) -> np.ndarray:
+             p_fp8: bool = False, local_window: int = 0) -> np.ndarray:
     """Jagged forward in float64.
 
     q [Tq, Hq, D], k/v [Tk, Hk, D]; seq_offsets for q and seq_offsets_k for
     k/v (None: the same). rab [B, Hq or 1, max_seq_len, max_seq_len] or None;
     mask (mask_type 3 only) [B, Hq or 1, max_seq_len, max_seq_len].
     p_fp8: the FP8 cast, P cast to E4M3 before the product with V (the
-    inputs are then E4M3 values, passed widened).
+    inputs are then E4M3 values, passed widened). local_window: the local
+    mask's window W (causal mask only; 0 = none).
     Returns out [Tq, Hq, D], or [len(rows), D] when ``rows`` lists (token, head) pairs.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -153,7 +154,8 @@ def hstu_fwd(q, k, v, seq_offsets, *, rab=None, mask=None, seq_offsets_k=None, n
     rc = _load().hstu_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(rab_a), _ptr(mask_a), _ptr(out), _ptr(off),
                                  _ptr(offk), _ptr(nc), _ptr(nt), B, max_seq_len, Hq, Hk, D,
                                  1 if rab_a is None else rab_a.shape[1], 1 if mask_a is None else mask_a.shape[1],
-                                 mask_type, target_group_size, float(alpha), float(out_scale), int(bool(p_fp8)),
+                                 mask_type, target_group_size, int(local_window), float(alpha), float(out_scale),
+                                 int(bool(p_fp8)),
                                  _ptr(rows_a), 0 if rows_a is None else rows_a.shape[0])
     if rc != 0:
         raise ValueError("oracle: invalid arguments")
@@ -162,7 +164,8 @@ def hstu_fwd(q, k, v, seq_offsets, *, rab=None, mask=None, seq_offsets_k=None, n
 
 def hstu_fwd_paged(q, k_new, v_new, kv_cache, seq_offsets_q, page_offsets, page_ids, last_page_len, *,
                    num_context=None, num_targets=None, mask_type: int = MASK_CAUSAL, target_group_size: int = 0,
-                   alpha: float = 1.0, out_scale: float, rows: Optional[Sequence] = None) -> np.ndarray:
+                   alpha: float = 1.0, out_scale: float, rows: Optional[Sequence] = None,
+                   local_window: int = 0) -> np.ndarray:
     """Paged forward in float64. kv_cache [num_pages, 2, page_size, Hk, D]."""
     q, kn, vn, kv = _f64(q), _f64(k_new), _f64(v_new), _f64(kv_cache)
     offq, poff, pids, lpl = _i64(seq_offsets_q), _i64(page_offsets), _i64(page_ids), _i64(last_page_len)
@@ -175,7 +178,7 @@ def hstu_fwd_paged(q, k_new, v_new, kv_cache, seq_offsets_q, page_offsets, page_
     out = np.zeros((Tq, Hq, D) if rows_a is None else (rows_a.shape[0], D), dtype=np.float64)
     rc = _load().hstu_oracle_fwd_paged(_ptr(q), _ptr(kn), _ptr(vn), _ptr(kv), _ptr(out), _ptr(offq), _ptr(poff),
                                        _ptr(pids), _ptr(lpl), _ptr(nc), _ptr(nt), B, page_size, Hq, Hk, D, mask_type,
-                                       target_group_size, float(alpha), float(out_scale), _ptr(rows_a),
+                                       target_group_size, int(local_window), float(alpha), float(out_scale), _ptr(rows_a),
                                        0 if rows_a is None else rows_a.shape[0])
     if rc != 0:
         raise ValueError("oracle: invalid arguments")

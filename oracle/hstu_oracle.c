@@ -42,6 +42,11 @@
  *     of the sequence is a candidate and the mask value m = mask[b,h,i,j]
  *     multiplies P; m == 0 removes the key entirely (it contributes exactly
  *     zero, whatever the score), as the built-in masks do;
+ *   - local mask (the feature table's local-mask row, which names the
+ *     feature only): a sliding window of W >= 1 positions on the causal
+ *     mask -- query i sees key j only when the causal mask above lets it and
+ *     i - j < W, for context, history and target pairs alike; W = 0 is no
+ *     window, and the window is defined for the causal mask only;
  *   - FP8 "cast" (the feature table's FP8 quantization row): element-level
  *     quantization with no scale. Q, K and V arrive as OCP E4M3 (FN) values
  *     (callers pass them widened to float64), and P = silu(...) is cast to
@@ -82,10 +87,13 @@ double hstu_oracle_e4m3(double x) {
 }
 
 /* Visibility of key j to query i, both positions local to one sequence of
- * length L, under the reading stated in the header comment. */
-int hstu_oracle_vis(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int64_t g, int64_t i, int64_t j) {
+ * length L, under the reading stated in the header comment (w: the local
+ * window, 0 for none). */
+int hstu_oracle_vis(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int64_t g, int64_t w, int64_t i,
+                    int64_t j) {
   if (i < 0 || j < 0 || i >= L || j >= L) return 0;
   if (mask_type != ORACLE_MASK_CAUSAL) return 1; /* none, or the user mask decides */
+  if (w > 0 && i - j >= w) return 0;             /* outside the local window */
   if (nt < 0) nt = 0;
   if (nt > L) nt = L;
   int64_t H = L - nt;
@@ -97,9 +105,9 @@ int hstu_oracle_vis(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int64_
 }
 
 /* Fill an L x L 0/1 matrix with hstu_oracle_vis. */
-void hstu_oracle_mask(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int64_t g, uint8_t* out) {
+void hstu_oracle_mask(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int64_t g, int64_t w, uint8_t* out) {
   for (int64_t i = 0; i < L; ++i)
-    for (int64_t j = 0; j < L; ++j) out[i * L + j] = (uint8_t)hstu_oracle_vis(mask_type, L, nc, nt, g, i, j);
+    for (int64_t j = 0; j < L; ++j) out[i * L + j] = (uint8_t)hstu_oracle_vis(mask_type, L, nc, nt, g, w, i, j);
 }
 
 /* One output row: query row qrow (pointer to D values), keys/values given as
@@ -107,11 +115,11 @@ void hstu_oracle_mask(int32_t mask_type, int64_t L, int64_t nc, int64_t nt, int6
 static void one_row(const double* qrow, const double* const* krows, const double* const* vrows,
                     const double* rabrow /* nullable, indexed by local j */,
                     const double* maskrow /* nullable (mask_type 3), indexed by local j */, int64_t L, int64_t D,
-                    int32_t mask_type, int64_t nc, int64_t nt, int64_t g, int64_t i, double alpha, double out_scale,
-                    int32_t p_fp8, double* out) {
+                    int32_t mask_type, int64_t nc, int64_t nt, int64_t g, int64_t w, int64_t i, double alpha,
+                    double out_scale, int32_t p_fp8, double* out) {
   for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
   for (int64_t j = 0; j < L; ++j) {
-    if (!hstu_oracle_vis(mask_type, L, nc, nt, g, i, j)) continue;
+    if (!hstu_oracle_vis(mask_type, L, nc, nt, g, w, i, j)) continue;
     if (maskrow && maskrow[j] == 0.0) continue;
     double s = 0.0;
     for (int64_t e = 0; e < D; ++e) s += qrow[e] * krows[j][e];
@@ -141,8 +149,10 @@ int hstu_oracle_fwd(const double* q, const double* k, const double* v, const dou
                     double* out, const int64_t* seq_offsets, const int64_t* seq_offsets_k,
                     const int64_t* num_context, const int64_t* num_targets, int64_t B, int64_t max_seq_len, int64_t Hq,
                     int64_t Hk, int64_t D, int64_t rab_heads, int64_t mask_heads, int32_t mask_type, int64_t g,
-                    double alpha, double out_scale, int32_t p_fp8, const int64_t* rows, int64_t n_rows) {
+                    int64_t local_window, double alpha, double out_scale, int32_t p_fp8, const int64_t* rows,
+                    int64_t n_rows) {
   if (B < 0 || Hq <= 0 || Hk <= 0 || D <= 0 || Hq % Hk != 0) return -1;
+  if (local_window < 0 || (local_window > 0 && mask_type != ORACLE_MASK_CAUSAL)) return -1;
   if ((mask_type == ORACLE_MASK_CUSTOM) != (mask != NULL)) return -1;
   if (rab && rab_heads != 1 && rab_heads != Hq) return -1;
   if (mask && mask_heads != 1 && mask_heads != Hq) return -1;
@@ -183,7 +193,8 @@ int hstu_oracle_fwd(const double* q, const double* k, const double* v, const dou
     const int64_t hr = rab_heads == 1 ? 0 : h, hm = mask_heads == 1 ? 0 : h;
     const double* rabrow = rab ? rab + ((b * rab_heads + hr) * max_seq_len + i) * max_seq_len : NULL;
     const double* maskrow = mask ? mask + ((b * mask_heads + hm) * max_seq_len + i) * max_seq_len : NULL;
-    one_row(q + (t * Hq + h) * D, kr, vr, rabrow, maskrow, L, D, mask_type, nc, nt, g, i, alpha, out_scale, p_fp8, o);
+    one_row(q + (t * Hq + h) * D, kr, vr, rabrow, maskrow, L, D, mask_type, nc, nt, g, local_window, i, alpha,
+            out_scale, p_fp8, o);
     free(kr);
     free(vr);
   }
@@ -204,9 +215,10 @@ int hstu_oracle_fwd_paged(const double* q, const double* k_new, const double* v_
                           double* out, const int64_t* seq_offsets_q, const int64_t* page_offsets,
                           const int64_t* page_ids, const int64_t* last_page_len, const int64_t* num_context,
                           const int64_t* num_targets, int64_t B, int64_t page_size, int64_t Hq, int64_t Hk, int64_t D,
-                          int32_t mask_type, int64_t g, double alpha, double out_scale, const int64_t* rows,
-                          int64_t n_rows) {
+                          int32_t mask_type, int64_t g, int64_t local_window, double alpha, double out_scale,
+                          const int64_t* rows, int64_t n_rows) {
   if (B < 0 || Hq <= 0 || Hk <= 0 || D <= 0 || Hq % Hk != 0 || page_size <= 0) return -1;
+  if (local_window < 0 || (local_window > 0 && mask_type != ORACLE_MASK_CAUSAL)) return -1;
   const int64_t Tq = seq_offsets_q[B];
   int64_t n_items = rows ? n_rows : Tq * Hq;
   int err = 0;
@@ -242,7 +254,8 @@ int hstu_oracle_fwd_paged(const double* q, const double* k_new, const double* v_
       kr[Lh + j] = k_new + ((q0 + j) * Hk + hk) * D;
       vr[Lh + j] = v_new + ((q0 + j) * Hk + hk) * D;
     }
-    one_row(q + (t * Hq + h) * D, kr, vr, NULL, NULL, L, D, mask_type, nc, nt, g, i, alpha, out_scale, 0, o);
+    one_row(q + (t * Hq + h) * D, kr, vr, NULL, NULL, L, D, mask_type, nc, nt, g, local_window, i, alpha, out_scale,
+            0, o);
     free(kr);
     free(vr);
   }

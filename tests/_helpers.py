@@ -41,6 +41,8 @@ def run_jagged(c, dev, out=None, workspace=None, **over) -> torch.Tensor:
               num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
               target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale, out=out,
               workspace=workspace)
+    if c.local_window:
+        kw["local_window"] = c.local_window
     kw.update(over)
     return hj.hstu_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets), **kw)
 
@@ -49,6 +51,8 @@ def run_paged(pc, dev, **over) -> torch.Tensor:
     kw = dict(num_context=pc.num_context, num_targets=pc.num_targets, max_seq_len=pc.max_seq_len,
               mask_type=pc.mask_type, target_group_size=pc.target_group_size, alpha=pc.alpha,
               out_scale=pc.out_scale)
+    if pc.local_window:
+        kw["local_window"] = pc.local_window
     kw.update(over)
     return hj.hstu_fwd_paged(pc.q.to(dev), pc.k_new.to(dev), pc.v_new.to(dev), pc.kv_cache.to(dev),
                              torch.as_tensor(pc.seq_offsets_q), torch.as_tensor(pc.page_offsets),
@@ -60,7 +64,8 @@ def oracle_jagged(c, rows=None) -> np.ndarray:
                            mask=None if c.mask is None else f64(c.mask), seq_offsets_k=c.seq_offsets_k,
                            num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
                            mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                           out_scale=c.out_scale, rows=rows, p_fp8=c.dtype == "fp8")
+                           out_scale=c.out_scale, rows=rows, p_fp8=c.dtype == "fp8",
+                           local_window=c.local_window)
 
 
 def oracle_jagged_sampled(c, picks):
@@ -81,7 +86,7 @@ def oracle_jagged_sampled(c, picks):
                                num_targets=None if c.num_targets is None else c.num_targets[b:b + 1],
                                max_seq_len=c.max_seq_len, mask_type=c.mask_type,
                                target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale,
-                               rows=rows, p_fp8=c.dtype == "fp8")
+                               rows=rows, p_fp8=c.dtype == "fp8", local_window=c.local_window)
         res[b] = (np.array([s0 + r for r, _ in rows]), np.array([h for _, h in rows]), vals)
     return res
 
@@ -91,7 +96,7 @@ def oracle_paged(pc, rows=None) -> np.ndarray:
                                  pc.page_offsets, pc.page_ids, pc.last_page_len, num_context=pc.num_context,
                                  num_targets=pc.num_targets, mask_type=pc.mask_type,
                                  target_group_size=pc.target_group_size, alpha=pc.alpha, out_scale=pc.out_scale,
-                                 rows=rows)
+                                 rows=rows, local_window=pc.local_window)
 
 
 def errors(got, ref):

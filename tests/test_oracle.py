@@ -130,9 +130,11 @@ def test_target_never_sees_other_groups():
 
 
 # ---------------------------------------------------------------- forward
-def small_case(seed, lengths, Hq=2, Hk=2, D=8, mask=CAUSAL, nc=None, nt=None, g=0, rab=False, S=None):
+def small_case(seed, lengths, Hq=2, Hk=2, D=8, mask=CAUSAL, nc=None, nt=None, g=0, rab=False, S=None,
+               local_window=0):
     return wl.jagged_case(seed, lengths, Hq, Hk, D, "f32", mask_type=mask, num_context=nc, num_targets=nt,
                           target_group_size=g, rab_std=0.5 if rab else None, max_seq_len=S, alpha=0.7,
+                          local_window=local_window,
                           out_scale=0.3)
 
 
@@ -140,7 +142,7 @@ def run_oracle(c, q=None, k=None, v=None, **over):
     kw = dict(rab=None if c.rab is None else f64(c.rab), mask=None if c.mask is None else f64(c.mask),
               seq_offsets_k=c.seq_offsets_k, num_context=c.num_context, num_targets=c.num_targets,
               max_seq_len=c.max_seq_len, mask_type=c.mask_type, target_group_size=c.target_group_size,
-              alpha=c.alpha, out_scale=c.out_scale)
+              alpha=c.alpha, out_scale=c.out_scale, local_window=c.local_window)
     kw.update(over)
     return oracle.hstu_fwd(f64(c.q) if q is None else q, f64(c.k) if k is None else k,
                            f64(c.v) if v is None else v, c.seq_offsets, **kw)
@@ -160,6 +162,8 @@ def dense_library(c):
         nc = 0 if c.num_context is None else c.num_context[b]
         nt = 0 if c.num_targets is None else c.num_targets[b]
         M = mask_from_rules(L, nc, nt, c.target_group_size, c.mask_type)
+        if c.local_window:
+            M &= window_band(L, c.local_window)
         for h in range(Hq):
             hk = h * Hk // Hq
             S = q[s0:s1, h, :] @ k[s0:s1, hk, :].T
@@ -626,7 +630,7 @@ def test_general_oracle_rejects_bad_arguments():
         oracle.hstu_fwd(f64(d.q), f64(d.k)[:8], f64(d.v)[:8], d.seq_offsets, seq_offsets_k=[0, 3, 8], max_seq_len=6)
 
 
-# ---------------------------------------------------------------- FP8 cast (row f3)
+# ---------------------------------------------------------------- FP8 cast
 E4M3 = torch.float8_e4m3fn
 
 
@@ -692,6 +696,8 @@ def dense_fp8(c):
         nc = 0 if c.num_context is None else c.num_context[b]
         nt = 0 if c.num_targets is None else c.num_targets[b]
         M = mask_from_rules(L, nc, nt, c.target_group_size, c.mask_type)
+        if c.local_window:
+            M &= window_band(L, c.local_window)
         for h in range(Hq):
             hk = h * Hk // Hq
             S = q[s0:s1, h, :] @ k[s0:s1, hk, :].T
@@ -739,3 +745,155 @@ def test_fp8_constant_rab_unit_values_closed_form():
     counts = closed_form_counts(L, nc, nt, g)
     np.testing.assert_allclose(out[:, 0, :], out_scale * p8 * np.repeat(np.asarray(counts, float)[:, None], D, 1),
                                rtol=1e-14)
+
+
+# ---------------------------------------------------------------- local mask
+def window_band(L, w):
+    """Pairs with i - j < w, from numpy's triangle routine (np.tri(L, L, -w)
+    marks exactly the pairs with j <= i - w)."""
+    return ~np.tri(L, L, -w, dtype=bool)
+
+
+def test_local_mask_bruteforce_random():
+    rng = np.random.default_rng(41)
+    for _ in range(400):
+        L = int(rng.integers(1, 40))
+        nc = int(rng.integers(-2, L + 4))
+        nt = int(rng.integers(-2, L + 4))
+        g = int(rng.choice([0, 1, 2, 3, 5]))
+        w = int(rng.integers(1, L + 3))
+        got = oracle.mask_matrix(CAUSAL, L, nc, nt, g, w)
+        ref = mask_from_rules(L, nc, nt, g, CAUSAL) & window_band(L, w)
+        np.testing.assert_array_equal(got, ref, err_msg=str((L, nc, nt, g, w)))
+
+
+def test_local_mask_hand_fixture():
+    # L = 7, two context rows, two targets in groups of one, window 3: the
+    # context rows see both context keys (the window bounds i - j only from
+    # above), history row 4 sees keys 2..4, target 6 sees history 4 and itself.
+    M = oracle.mask_matrix(CAUSAL, 7, 2, 2, 1, 3).astype(int)
+    expect = np.array([[1, 1, 0, 0, 0, 0, 0],
+                       [1, 1, 0, 0, 0, 0, 0],
+                       [1, 1, 1, 0, 0, 0, 0],
+                       [0, 1, 1, 1, 0, 0, 0],
+                       [0, 0, 1, 1, 1, 0, 0],
+                       [0, 0, 0, 1, 1, 1, 0],
+                       [0, 0, 0, 0, 1, 0, 1]])
+    np.testing.assert_array_equal(M, expect)
+
+
+def closed_form_counts_window(L, nc, nt, g, w):
+    """Row counts with the window, from interval lengths: each row's set is
+    one or two intervals of keys, cut below at lo = max(0, i - w + 1)."""
+    nt = min(max(nt, 0), L)
+    H = L - nt
+    nc = min(max(nc, 0), H)
+    out = []
+    for i in range(L):
+        lo = max(0, i - w + 1)
+        if i < nc:
+            out.append(nc - lo)
+        elif i < H or g == 0:
+            out.append(min(i + 1, w))
+        else:
+            start = H + (i - H) // g * g
+            out.append(max(0, H - lo) + i + 1 - max(start, lo))
+    return np.array(out)
+
+
+def test_local_mask_row_counts_closed_form():
+    rng = np.random.default_rng(42)
+    for _ in range(300):
+        L = int(rng.integers(1, 60))
+        nc, nt = int(rng.integers(0, L + 2)), int(rng.integers(0, L + 2))
+        g = int(rng.choice([0, 1, 3, 4]))
+        w = int(rng.integers(1, 70))
+        M = oracle.mask_matrix(CAUSAL, L, nc, nt, g, w)
+        np.testing.assert_array_equal(M.sum(1), closed_form_counts_window(L, nc, nt, g, w), err_msg=str((L, nc, nt, g, w)))
+
+
+def test_local_window_covering_the_sequence_is_no_window():
+    for (L, nc, nt, g) in [(17, 3, 5, 2), (30, 0, 0, 0), (9, 9, 0, 0)]:
+        for w in (L, L + 1, 4 * L):
+            np.testing.assert_array_equal(oracle.mask_matrix(CAUSAL, L, nc, nt, g, w),
+                                          oracle.mask_matrix(CAUSAL, L, nc, nt, g))
+
+
+def test_local_window_one_reads_only_the_diagonal():
+    # With no context, a window of one leaves each query its own key:
+    # O_i = out_scale * silu(alpha (q_i . k_i + rab_ii)) v_i, by hand.
+    c = small_case(43, [13, 1, 20], Hq=4, Hk=2, nt=(0, 7), g=1, rab=True)
+    got = run_oracle(c, local_window=1)
+    q, k, v, rab = f64(c.q), f64(c.k), f64(c.v), f64(c.rab)
+    ref = np.zeros_like(q)
+    for b in range(c.batch):
+        s0, s1 = c.seq_offsets[b], c.seq_offsets[b + 1]
+        for i in range(s1 - s0):
+            for h in range(4):
+                x = c.alpha * (q[s0 + i, h] @ k[s0 + i, h // 2] + rab[b, h, i, i])
+                ref[s0 + i, h] = c.out_scale * x * expit(x) * v[s0 + i, h // 2]
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", ["w5", "w1_ctx", "w9_ctx_tgt_g3_rab", "w16_gqa_delta"])
+def test_local_oracle_matches_dense_library(kind):
+    if kind == "w5":
+        c = small_case(44, [13, 1, 20, 0], local_window=5)
+    elif kind == "w1_ctx":
+        c = small_case(45, [19, 24, 7], nc=(0, 5), local_window=1)
+    elif kind == "w9_ctx_tgt_g3_rab":
+        c = small_case(46, [19, 24, 7], nc=(0, 5), nt=(0, 9), g=3, rab=True, S=30, local_window=9)
+    else:
+        full = small_case(47, [40, 33], Hq=6, Hk=2, nt=(0, 5), g=1, rab=True, local_window=16)
+        ref = dense_library(full)
+        lq = np.array([7, 12])
+        rows = np.concatenate([np.arange(full.seq_offsets[b + 1] - lq[b], full.seq_offsets[b + 1]) for b in range(2)])
+        offq = np.concatenate([[0], np.cumsum(lq)])
+        got = oracle.hstu_fwd(f64(full.q)[rows], f64(full.k), f64(full.v), offq, seq_offsets_k=full.seq_offsets,
+                              rab=f64(full.rab), num_targets=full.num_targets, max_seq_len=full.max_seq_len,
+                              mask_type=CAUSAL, target_group_size=1, alpha=full.alpha, out_scale=full.out_scale,
+                              local_window=16)
+        np.testing.assert_allclose(got, ref[rows], rtol=1e-12, atol=1e-13)
+        return
+    np.testing.assert_allclose(run_oracle(c), dense_library(c), rtol=1e-12, atol=1e-13)
+
+
+def test_local_window_paged_equals_gathered_jagged():
+    pc = wl.paged_case(48, [70, 0, 129, 64], [3, 5, 1, 4], 4, 2, 16, "f32", page_size=32, num_context=(0, 6),
+                       target_group_size=2, extra_pages=3, local_window=40)
+    out = oracle.hstu_fwd_paged(f64(pc.q), f64(pc.k_new), f64(pc.v_new), f64(pc.kv_cache), pc.seq_offsets_q,
+                                pc.page_offsets, pc.page_ids, pc.last_page_len, num_context=pc.num_context,
+                                num_targets=pc.num_targets, mask_type=CAUSAL, target_group_size=2, alpha=pc.alpha,
+                                out_scale=pc.out_scale, local_window=40)
+    assert np.all(np.isfinite(out))
+    K, V, off = gather_paged(pc)
+    Q = np.zeros((K.shape[0], 4, 16))
+    for b in range(pc.batch):
+        q0, q1 = pc.seq_offsets_q[b], pc.seq_offsets_q[b + 1]
+        Q[off[b] + pc.history_lengths[b]: off[b + 1]] = f64(pc.q)[q0:q1]
+    ref = oracle.hstu_fwd(Q, K, V, off, num_context=pc.num_context, num_targets=pc.num_targets,
+                          max_seq_len=int(np.diff(off).max()), mask_type=CAUSAL, target_group_size=2,
+                          alpha=pc.alpha, out_scale=pc.out_scale, local_window=40)
+    for b in range(pc.batch):
+        q0, q1 = pc.seq_offsets_q[b], pc.seq_offsets_q[b + 1]
+        np.testing.assert_array_equal(out[q0:q1], ref[off[b] + pc.history_lengths[b]: off[b + 1]])
+
+
+def test_local_window_metrics_counts_match_oracle_mask():
+    from hstu_jagged_attention_amd import metrics
+    rng = np.random.default_rng(49)
+    for _ in range(150):
+        L = int(rng.integers(0, 50))
+        nc, nt, g = int(rng.integers(0, L + 2)), int(rng.integers(0, L + 2)), int(rng.choice([0, 1, 3]))
+        w = int(rng.integers(1, 60))
+        M = oracle.mask_matrix(CAUSAL, L, nc, nt, g, w)
+        np.testing.assert_array_equal(metrics.visible_per_row(L, nc, nt, g, CAUSAL, w), M.sum(1))
+
+
+def test_local_window_rejected_outside_the_causal_mask():
+    c = small_case(50, [5, 6], mask=NONE)
+    with pytest.raises(ValueError):
+        run_oracle(c, local_window=3)
+    d = small_case(51, [5, 6])
+    with pytest.raises(ValueError):
+        run_oracle(d, local_window=-1)
