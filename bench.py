@@ -45,7 +45,7 @@ FLUSH_BYTES = 1 << 30  # written before each cold step: > 256 MB Infinity Cache 
 # priced against the fp32 MFMA peak.
 BOUND = {"tiny_fp32_bidirectional": "mfma", "bf16_mha_causal": "mfma", "fp16_gqa_causal": "mfma",
          "bf16_rab_target": "hbm", "bf16_paged_target": "hbm", "bf16_custom_mask": "hbm", "bf16_delta_qk": "hbm",
-         "fp8_gqa_causal": "mfma"}
+         "fp8_gqa_causal": "mfma", "fp16_gqa_local": "mfma"}
 
 
 def parse():
@@ -259,7 +259,7 @@ def workload_work(name, c):
     E = ELEM[c.dtype]
     if name == "bf16_paged_target":
         pairs = metrics.pairs_paged(c.history_lengths, c.new_lengths, c.num_context, c.num_targets,
-                                    c.target_group_size, c.mask_type)
+                                    c.target_group_size, c.mask_type, c.local_window)
         Tq = int(c.seq_offsets_q[-1])
         alg_bytes = metrics.algorithmic_bytes_paged(Tq, int(c.history_lengths.sum()), c.num_heads_q, c.num_heads_kv,
                                                     c.head_dim, E)
@@ -278,10 +278,10 @@ def workload_work(name, c):
         else:
             if c.seq_offsets_k is None:
                 pairs = metrics.pairs_jagged(c.seq_offsets, c.num_context, c.num_targets, c.target_group_size,
-                                             c.mask_type)
+                                             c.mask_type, c.local_window)
             else:
                 pairs = metrics.pairs_delta(c.key_lengths, c.lengths, c.num_context, c.num_targets,
-                                            c.target_group_size, c.mask_type)
+                                            c.target_group_size, c.mask_type, c.local_window)
             alg_bytes = metrics.algorithmic_bytes_jagged(T, c.num_heads_q, c.num_heads_kv, c.head_dim, E,
                                                          pairs if c.rab is not None else 0, Tk=Tk,
                                                          out_bytes=OUT_ELEM.get(c.dtype))
@@ -296,6 +296,8 @@ def workload_work(name, c):
     desc.update(num_heads_q=c.num_heads_q, num_heads_kv=c.num_heads_kv, head_dim=c.head_dim,
                 mask={0: "causal", 2: "bidirectional", 3: "user mask"}[c.mask_type],
                 rab=bool(getattr(c, "rab", None) is not None), visible_pairs_per_head=pairs)
+    if c.local_window:
+        desc.update(local_window=c.local_window)
     return flops, alg_bytes, desc
 
 
@@ -309,16 +311,16 @@ def build_step(name, dev):
                                     torch.as_tensor(c.seq_offsets_q), torch.as_tensor(c.page_offsets),
                                     torch.as_tensor(c.page_ids), torch.as_tensor(c.last_page_len),
                                     num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
-                                    mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                                    out_scale=c.out_scale)
+                                    mask_type=c.mask_type, target_group_size=c.target_group_size,
+                                    local_window=c.local_window, alpha=c.alpha, out_scale=c.out_scale)
     else:
         prep = hj.prepare_fwd(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets),
                               rab=None if c.rab is None else c.rab.to(dev),
                               mask=None if c.mask is None else c.mask.to(dev),
                               seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
                               num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
-                              mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                              out_scale=c.out_scale)
+                              mask_type=c.mask_type, target_group_size=c.target_group_size,
+                              local_window=c.local_window, alpha=c.alpha, out_scale=c.out_scale)
     flops, alg_bytes, desc = workload_work(name, c)
     return c, prep, flops, alg_bytes, desc
 
@@ -357,7 +359,8 @@ def oracle_sample(c, name, flops_full, stride):
                 Lh = int(c.history_lengths[b])
                 nc = 0 if c.num_context is None else int(c.num_context[b])
                 nt = 0 if c.num_targets is None else int(c.num_targets[b])
-                per_row = metrics.visible_per_row(Lh + q1 - q0, nc, nt, c.target_group_size, c.mask_type)
+                per_row = metrics.visible_per_row(Lh + q1 - q0, nc, nt, c.target_group_size, c.mask_type,
+                                                  c.local_window)
                 for t in range(q0, q1, stride):
                     rows += [(t, h) for h in range(c.num_heads_q)]
                     pairs += int(per_row[Lh + t - q0]) * c.num_heads_q
@@ -365,7 +368,8 @@ def oracle_sample(c, name, flops_full, stride):
         run = lambda: oracle.hstu_fwd_paged(q, kn, vn, kv, c.seq_offsets_q, c.page_offsets, c.page_ids,
                                             c.last_page_len, num_context=c.num_context, num_targets=c.num_targets,
                                             mask_type=c.mask_type, target_group_size=c.target_group_size,
-                                            alpha=c.alpha, out_scale=c.out_scale, rows=rows)
+                                            alpha=c.alpha, out_scale=c.out_scale, rows=rows,
+                                            local_window=c.local_window)
         return run, fl, desc
     q, k, v = f64(c.q), f64(c.k), f64(c.v)
     rab = None if c.rab is None else f64(c.rab)
@@ -391,14 +395,15 @@ def oracle_sample(c, name, flops_full, stride):
             else:
                 nc = 0 if c.num_context is None else int(c.num_context[b])
                 nt = 0 if c.num_targets is None else int(c.num_targets[b])
-                per_row = metrics.visible_per_row(Lk, nc, nt, c.target_group_size, c.mask_type)
+                per_row = metrics.visible_per_row(Lk, nc, nt, c.target_group_size, c.mask_type, c.local_window)
                 pairs += int(per_row[pos].sum()) * c.num_heads_q
         fl = 4.0 * c.head_dim * pairs
         desc = f"every {stride}th query row of every sequence, all heads"
     run = lambda: oracle.hstu_fwd(q, k, v, c.seq_offsets, rab=rab, mask=mask, seq_offsets_k=c.seq_offsets_k,
                                   num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
                                   mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha,
-                                  out_scale=c.out_scale, rows=rows, p_fp8=c.dtype == "fp8")
+                                  out_scale=c.out_scale, rows=rows, p_fp8=c.dtype == "fp8",
+                                  local_window=c.local_window)
     return run, fl, desc
 
 
@@ -418,7 +423,7 @@ def _time_for(run, seconds):
 # (one thread) of CPU time.
 ORACLE_STRIDES = {"tiny_fp32_bidirectional": (1, 1), "bf16_mha_causal": (1, 8), "bf16_rab_target": (16, 128),
                   "fp16_gqa_causal": (16, 128), "bf16_paged_target": (1, 8), "bf16_custom_mask": (1, 8),
-                  "bf16_delta_qk": (1, 8), "fp8_gqa_causal": (16, 128)}
+                  "bf16_delta_qk": (1, 8), "fp8_gqa_causal": (16, 128), "fp16_gqa_local": (4, 32)}
 
 
 def cpu_baseline(c, name, flops_full):
@@ -575,7 +580,8 @@ def main():
         copy_calibration(dev)
         return
     names = ["tiny_fp32_bidirectional", "bf16_mha_causal", "bf16_rab_target", "fp16_gqa_causal",
-             "bf16_paged_target", "bf16_custom_mask", "bf16_delta_qk", "fp8_gqa_causal"] if args.all \
+             "bf16_paged_target", "bf16_custom_mask", "bf16_delta_qk", "fp8_gqa_causal", "fp16_gqa_local"] \
+        if args.all \
         else [args.workload]
     for name in names:
         print(f"[bench] {name}: building inputs", file=sys.stderr, flush=True)

@@ -72,19 +72,19 @@ def load_library(path: Optional[str] = None):
     lib.hstu_fwd_workspace_size.restype = SZ
     lib.hstu_fwd_paged_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, E]
     lib.hstu_fwd_paged_workspace_size.restype = SZ
-    jag = [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, E, I32, F, F, E, P, SZ, P]
-    pag = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, F, F, E, P, SZ, P]
+    jag = [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, E, I32, I32, F, F, E, P, SZ, P]
+    pag = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, I32, F, F, E, P, SZ, P]
     for name in ("hstu_fwd", "hstu_fwd_run"):
         getattr(lib, name).argtypes = jag
         getattr(lib, name).restype = E
     for name in ("hstu_fwd_paged", "hstu_fwd_paged_run"):
         getattr(lib, name).argtypes = pag
         getattr(lib, name).restype = E
-    lib.hstu_fwd_noalloc.argtypes = jag[:22] + [P]
+    lib.hstu_fwd_noalloc.argtypes = jag[:23] + [P]
     lib.hstu_fwd_noalloc.restype = E
-    lib.hstu_fwd_plan.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
+    lib.hstu_fwd_plan.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, E, I32, I32, E, P, SZ, P]
     lib.hstu_fwd_plan.restype = E
-    lib.hstu_fwd_paged_plan.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, E, P, SZ, P]
+    lib.hstu_fwd_paged_plan.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, E, I32, I32, E, P, SZ, P]
     lib.hstu_fwd_paged_plan.restype = E
     lib.hstu_status_string.argtypes = [E]
     lib.hstu_status_string.restype = ctypes.c_char_p
@@ -180,14 +180,16 @@ class Prepared:
 def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, *, rab: Optional[torch.Tensor] = None,
                 mask: Optional[torch.Tensor] = None, seq_offsets_k=None, num_context=None, num_targets=None,
                 max_seq_len: Optional[int] = None, mask_type: Optional[int] = None, target_group_size: int = 0,
-                alpha: float = 1.0, out_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> Prepared:
+                local_window: int = 0, alpha: float = 1.0, out_scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> Prepared:
     """Marshal a jagged forward: q [Tq, Hq, D], k/v [Tk, Hk, D] on the GPU.
 
     seq_offsets addresses q; seq_offsets_k (optional) addresses k/v when the
     query and key lengths differ (queries are the last positions of each
     sequence). rab and mask are [B, Hq or 1, max_seq_len, max_seq_len].
     mask_type defaults to MASK_CUSTOM when a mask is given, else MASK_CAUSAL.
+    local_window (causal mask only) is the local mask's window W: key j is
+    visible to query i only when i - j < W as well (0: no window).
     max_seq_len (the page's maximum sequence length: the row stride of rab
     and mask, and the bound on every key sequence) is required: the binding
     never reads device arrays back."""
@@ -238,9 +240,10 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offsets, 
     stream = _stream(device)
     fwd_args = (_ptr(q), _ptr(k), _ptr(v), _ptr(rab), _ptr(mask), _ptr(out), _ptr(off), _ptr(offk), _ptr(nc),
                 _ptr(nt), B, max_seq_len, Hq, Hk, D, heads["rab"], heads["mask"], int(mask_type),
-                int(target_group_size), float(alpha), float(out_scale), code, _ptr(workspace), wsb, stream)
+                int(target_group_size), int(local_window), float(alpha), float(out_scale), code, _ptr(workspace),
+                wsb, stream)
     plan_args = (_ptr(off), _ptr(offk), _ptr(nc), _ptr(nt), B, max_seq_len, Hq, Hk, D, int(mask_type),
-                 int(target_group_size), code, _ptr(workspace), wsb, stream)
+                 int(target_group_size), int(local_window), code, _ptr(workspace), wsb, stream)
     return Prepared("hstu_fwd", lib, fwd_args, plan_args, out, workspace, (q, k, v, rab, mask, off, offk, nc, nt))
 
 
@@ -257,7 +260,7 @@ def hstu_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offs
     the call itself to allocate nothing). Keywords as prepare_fwd."""
     prep = prepare_fwd(q, k, v, seq_offsets, out=out, workspace=torch.empty(0, dtype=torch.uint8, device=q.device),
                        **kw)
-    st = prep._lib.hstu_fwd_noalloc(*prep._fwd_args[:22], prep._fwd_args[24])
+    st = prep._lib.hstu_fwd_noalloc(*prep._fwd_args[:23], prep._fwd_args[-1])
     if st != HSTU_OK:
         raise HstuError(st, "hstu_fwd_noalloc")
     return out
@@ -266,8 +269,8 @@ def hstu_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_offs
 def prepare_fwd_paged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, kv_cache: torch.Tensor,
                       seq_offsets_q, page_offsets, page_ids, last_page_len, *, num_context=None, num_targets=None,
                       max_seq_len: Optional[int] = None, mask_type: int = MASK_CAUSAL, target_group_size: int = 0,
-                      alpha: float = 1.0, out_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None) -> Prepared:
+                      local_window: int = 0, alpha: float = 1.0, out_scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> Prepared:
     """Marshal a paged-KV forward. kv_cache [num_pages, 2, page_size, Hk, D].
 
     max_seq_len (the bound on history + new tokens of every request) is
@@ -306,9 +309,10 @@ def prepare_fwd_paged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
     stream = _stream(device)
     fwd_args = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(offq), _ptr(kv_cache), _ptr(poff), _ptr(pids),
                 _ptr(lpl), _ptr(nc), _ptr(nt), B, page_size, max_seq_len, Hq, Hk, D, int(mask_type),
-                int(target_group_size), float(alpha), float(out_scale), code, _ptr(workspace), wsb, stream)
+                int(target_group_size), int(local_window), float(alpha), float(out_scale), code, _ptr(workspace),
+                wsb, stream)
     plan_args = (_ptr(offq), _ptr(poff), _ptr(lpl), _ptr(nc), _ptr(nt), B, page_size, max_seq_len, Hq, Hk, D,
-                 int(mask_type), int(target_group_size), code, _ptr(workspace), wsb, stream)
+                 int(mask_type), int(target_group_size), int(local_window), code, _ptr(workspace), wsb, stream)
     return Prepared("hstu_fwd_paged", lib, fwd_args, plan_args, out, workspace,
                     (q, k_new, v_new, kv_cache, offq, poff, pids, lpl, nc, nt))
 

@@ -43,9 +43,10 @@ hstu::DType to_internal(hstu_dtype_t dt) {
 
 // Checks shared by both entry points. Returns HSTU_OK or the error.
 hstu_status_t check_common(int32_t batch, int32_t max_seq_len, int32_t hq, int32_t hk, int32_t d, hstu_mask_t mask,
-                           int32_t group_size, hstu_dtype_t dtype, const int32_t* num_context,
+                           int32_t group_size, int32_t local_window, hstu_dtype_t dtype, const int32_t* num_context,
                            const int32_t* num_targets) {
-  if (batch < 0 || hq < 0 || d < 0 || hk < 0 || max_seq_len < 0 || group_size < 0) return HSTU_ERR_INVALID_ARG;
+  if (batch < 0 || hq < 0 || d < 0 || hk < 0 || max_seq_len < 0 || group_size < 0 || local_window < 0)
+    return HSTU_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return HSTU_ERR_UNSUPPORTED;
   if (mask != HSTU_MASK_CAUSAL && mask != HSTU_MASK_NONE && mask != HSTU_MASK_CUSTOM) {
     return mask == 1 ? HSTU_ERR_UNSUPPORTED : HSTU_ERR_INVALID_ARG;
@@ -55,7 +56,7 @@ hstu_status_t check_common(int32_t batch, int32_t max_seq_len, int32_t hq, int32
   if (hk <= 0 || hq % hk != 0) return HSTU_ERR_INVALID_ARG;
   if (max_seq_len < 1 || max_seq_len > kMaxSeqLen) return HSTU_ERR_INVALID_ARG;
   if (!head_dim_ok(d, dtype)) return HSTU_ERR_UNSUPPORTED;
-  if (mask != HSTU_MASK_CAUSAL && (num_context || num_targets)) return HSTU_ERR_INVALID_ARG;
+  if (mask != HSTU_MASK_CAUSAL && (num_context || num_targets || local_window > 0)) return HSTU_ERR_INVALID_ARG;
   if ((num_context && !aligned4(num_context)) || (num_targets && !aligned4(num_targets))) return HSTU_ERR_INVALID_ARG;
   return HSTU_OK;
 }
@@ -125,14 +126,14 @@ hstu_status_t enqueue(const hstu::FwdArgs& a, int phase) {
 // scratch: the workspace is the library's static device scratch (the
 // allocation-free entry point); its layout is then sized to fit it.
 hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, const void* rab, const void* mask,
-                     void* out, const int32_t* seq_offsets, const int32_t* seq_offsets_k,
-                     const int32_t* num_context, const int32_t* num_targets, int32_t batch, int32_t max_seq_len,
-                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads,
-                     int32_t mask_num_heads, hstu_mask_t mask_type, int32_t target_group_size, float alpha,
+                     void* out, const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
+                     const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
+                     int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
+                     hstu_mask_t mask_type, int32_t target_group_size, int32_t local_window, float alpha,
                      float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream,
                      bool scratch = false) {
   hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
-                                  target_group_size, dtype, num_context, num_targets);
+                                  target_group_size, local_window, dtype, num_context, num_targets);
   if (st != HSTU_OK) return st;
   if (batch == 0 || num_heads_q == 0 || head_dim == 0) return HSTU_OK;
   if (mask_type == HSTU_MASK_CUSTOM && dtype == HSTU_F32) return HSTU_ERR_UNSUPPORTED;
@@ -181,6 +182,7 @@ hstu_status_t jagged(int phase, const void* q, const void* k, const void* v, con
   a.num_heads_kv = num_heads_kv;
   a.head_dim = head_dim;
   a.target_group_size = target_group_size;
+  a.local_window = local_window;
   a.alpha = alpha;
   a.out_scale = out_scale;
   a.workspace = workspace;
@@ -195,10 +197,10 @@ hstu_status_t paged(int phase, const void* q, const void* k_new, const void* v_n
                     const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
                     const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                    int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    int32_t target_group_size, int32_t local_window, float alpha, float out_scale, hstu_dtype_t dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
-                                  target_group_size, dtype, num_context, num_targets);
+                                  target_group_size, local_window, dtype, num_context, num_targets);
   if (st != HSTU_OK) return st;
   if (mask_type == HSTU_MASK_CUSTOM) return HSTU_ERR_UNSUPPORTED;  // the user mask is built for jagged calls
   if (dtype == HSTU_FP8_E4M3 && batch > 0 && num_heads_q > 0 && head_dim > 0)
@@ -241,6 +243,7 @@ hstu_status_t paged(int phase, const void* q, const void* k_new, const void* v_n
   a.num_heads_kv = num_heads_kv;
   a.head_dim = head_dim;
   a.target_group_size = target_group_size;
+  a.local_window = local_window;
   a.alpha = alpha;
   a.out_scale = out_scale;
   a.workspace = workspace;
@@ -257,11 +260,11 @@ hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* 
                        const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
                        const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
                        int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
-                       hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
-                       hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                       hstu_mask_t mask_type, int32_t target_group_size, int32_t local_window, float alpha,
+                       float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return jagged(kBoth, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
                 max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
-                target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
+                target_group_size, local_window, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 hstu_status_t hstu_fwd_noalloc(const void* q, const void* k, const void* v, const void* rab, const void* mask,
@@ -269,38 +272,39 @@ hstu_status_t hstu_fwd_noalloc(const void* q, const void* k, const void* v, cons
                                const int32_t* num_context, const int32_t* num_targets, int32_t batch,
                                int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                                int32_t rab_num_heads, int32_t mask_num_heads, hstu_mask_t mask_type,
-                               int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
-                               void* stream) {
+                               int32_t target_group_size, int32_t local_window, float alpha, float out_scale,
+                               hstu_dtype_t dtype, void* stream) {
   // Empty inputs and argument errors are reported before the scratch is touched.
   hstu_status_t st = check_common(batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
-                                  target_group_size, dtype, num_context, num_targets);
+                                  target_group_size, local_window, dtype, num_context, num_targets);
   if (st != HSTU_OK || batch == 0 || num_heads_q == 0 || head_dim == 0) return st;
   void* ws = nullptr;
   size_t ws_bytes = 0;
   if (hstu::scratch_workspace(&ws, &ws_bytes) != hipSuccess) return HSTU_ERR_HIP;
   return jagged(kBoth, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
                 max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
-                target_group_size, alpha, out_scale, dtype, ws, ws_bytes, stream, true);
+                target_group_size, local_window, alpha, out_scale, dtype, ws, ws_bytes, stream, true);
 }
 
 hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
                             const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
                             int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size,
-                            hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                            int32_t local_window, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   return jagged(kPlan, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seq_offsets, seq_offsets_k, num_context,
                 num_targets, batch, max_seq_len, num_heads_q, num_heads_kv, head_dim, 0, 0, mask_type,
-                target_group_size, 1.0f, 1.0f, dtype, workspace, workspace_bytes, stream);
+                target_group_size, local_window, 1.0f, 1.0f, dtype, workspace, workspace_bytes, stream);
 }
 
 hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
                            const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
                            const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
                            int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
-                           hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
-                           hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                           hstu_mask_t mask_type, int32_t target_group_size, int32_t local_window, float alpha,
+                           float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return jagged(kRun, q, k, v, rab, mask, out, seq_offsets, seq_offsets_k, num_context, num_targets, batch,
                 max_seq_len, num_heads_q, num_heads_kv, head_dim, rab_num_heads, mask_num_heads, mask_type,
-                target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
+                target_group_size, local_window, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new, void* out,
@@ -308,22 +312,22 @@ hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new
                              const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
                              const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                             int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t target_group_size, int32_t local_window, float alpha, float out_scale,
+                             hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return paged(kBoth, q, k_new, v_new, out, seq_offsets_q, kv_cache, page_offsets, page_ids, last_page_len,
                num_context, num_targets, batch, page_size, max_seq_len, num_heads_q, num_heads_kv, head_dim,
-               mask_type, target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
+               mask_type, target_group_size, local_window, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 hstu_status_t hstu_fwd_paged_plan(const int32_t* seq_offsets_q, const int32_t* page_offsets,
                                   const int32_t* last_page_len, const int32_t* num_context, const int32_t* num_targets,
                                   int32_t batch, int32_t page_size, int32_t max_seq_len, int32_t num_heads_q,
                                   int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                                  int32_t target_group_size, hstu_dtype_t dtype, void* workspace,
+                                  int32_t target_group_size, int32_t local_window, hstu_dtype_t dtype, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  return paged(kPlan, nullptr, nullptr, nullptr, nullptr, seq_offsets_q, nullptr, page_offsets, nullptr,
-               last_page_len, num_context, num_targets, batch, page_size, max_seq_len, num_heads_q, num_heads_kv,
-               head_dim, mask_type, target_group_size, 1.0f, 1.0f, dtype, workspace, workspace_bytes, stream);
+  return paged(kPlan, nullptr, nullptr, nullptr, nullptr, seq_offsets_q, nullptr, page_offsets, nullptr, last_page_len,
+               num_context, num_targets, batch, page_size, max_seq_len, num_heads_q, num_heads_kv, head_dim, mask_type,
+               target_group_size, local_window, 1.0f, 1.0f, dtype, workspace, workspace_bytes, stream);
 }
 
 hstu_status_t hstu_fwd_paged_run(const void* q, const void* k_new, const void* v_new, void* out,
@@ -331,11 +335,11 @@ hstu_status_t hstu_fwd_paged_run(const void* q, const void* k_new, const void* v
                                  const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
                                  const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
                                  int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                                 int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 int32_t target_group_size, int32_t local_window, float alpha, float out_scale,
+                                 hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return paged(kRun, q, k_new, v_new, out, seq_offsets_q, kv_cache, page_offsets, page_ids, last_page_len,
                num_context, num_targets, batch, page_size, max_seq_len, num_heads_q, num_heads_kv, head_dim,
-               mask_type, target_group_size, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
+               mask_type, target_group_size, local_window, alpha, out_scale, dtype, workspace, workspace_bytes, stream);
 }
 
 const char* hstu_status_string(hstu_status_t status) {

@@ -40,6 +40,7 @@ struct FwdArgs {
   int32_t rab_heads;   // 1 (one rab for every head) or num_heads_q
   int32_t mask_heads;  // 1 or num_heads_q
   int32_t target_group_size;
+  int32_t local_window;  // local mask window W (causal only), 0: none
   float alpha;
   float out_scale;
   void* workspace;

@@ -5,7 +5,9 @@
 // head, O = out_scale * (M .* silu(alpha * (Q K^T + rab))) V over jagged
 // sequences, MHA or GQA, with the bidirectional mask, the causal mask built
 // from num_context / num_targets / target_group_size, or the user's mask
-// tensor (mask_type 3, whose values multiply P); rab may be shared by all
+// tensor (mask_type 3, whose values multiply P), optionally narrowed by a
+// local window (the feature table's local-mask row: key j is visible to
+// query i only when i - j < W as well); rab may be shared by all
 // heads ([B, 1, S, S]); queries may be the last positions of longer key
 // sequences (seq_offsets_k); and a paged variant reads history K/V from
 // kv_cache pages. No softmax: partial sums over key tiles add exactly, so no
@@ -104,6 +106,7 @@ struct KParams {
                         // full (q tile descending, sequence, head group) grid
   int32_t ps_log2;    // log2(page_size)
   int32_t g;          // target_group_size
+  int32_t win;        // local window W (causal mask only), 0: none
   int32_t rab_vec;    // rab rows allow 4-element vector loads
   int32_t rab_heads;  // 1: one rab (and mask_heads 1: one mask) for every query head
   int32_t mask_heads;
@@ -160,15 +163,18 @@ __device__ inline Seq load_seq(const KParams& p, int b, bool causal) {
 }
 
 // Key tiles that are not fully masked for the query rows [i_lo, i_hi]
-// (absolute positions): tiles [0, ta) then [tb0, tb1).
+// (absolute positions): tiles [t0, ta) then [tb0, tb1).
 // Rows below H see keys up to max(i, nc - 1); target rows see all of
 // [0, H) and, causally, their own group of g targets (all targets if g = 0).
+// A local window W hides the keys below i - W + 1 from row i, so no row of
+// the range sees a key below i_lo - W + 1.
 struct Tiles {
-  int ta, tb0, tb1;
+  int t0, ta, tb0, tb1;
 };
 
-__device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, bool causal, int bn) {
+__device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, int win, bool causal, int bn) {
   Tiles t;
+  t.t0 = 0;
   if (!causal) {
     t.ta = (s.L + bn - 1) / bn;
     t.tb0 = t.tb1 = t.ta;
@@ -184,10 +190,19 @@ __device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, bool
     b_lo = s.H + ((max(i_lo, s.H) - s.H) / g) * g;
     b_end = i_hi + 1;
   }
+  const int w_lo = win > 0 ? max(i_lo - win + 1, 0) : 0;  // first key inside some row's window
   t.ta = (a_end + bn - 1) / bn;
-  t.tb0 = max(b_lo / bn, t.ta);
+  t.t0 = min(w_lo / bn, t.ta);
+  t.tb0 = max(max(b_lo, w_lo) / bn, t.ta);
   t.tb1 = max((b_end + bn - 1) / bn, t.tb0);
   return t;
+}
+
+// Number of tiles in the range, and its n-th tile.
+__device__ inline int tile_count(const Tiles& t) { return (t.ta - t.t0) + (t.tb1 - t.tb0); }
+__device__ inline int nth_tile(const Tiles& t, int n) {
+  const int na = t.ta - t.t0;
+  return n < na ? t.t0 + n : t.tb0 + (n - na);
 }
 
 // ------------------------------------------------------------------------
@@ -256,7 +271,6 @@ constexpr int kMinChunkTiles = 4;
 constexpr int kCostCache = 4096;  // items whose cost the planner keeps in LDS
 constexpr int kSeqCache = 2048;   // sequences whose lengths the planner keeps in LDS
 
-__device__ inline int item_cost(const Tiles& t) { return t.ta + t.tb1 - t.tb0; }
 
 template <bool PAGED>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, int causal) {
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
     const int q_lo = qt * p.bm;
     if (q_lo >= s.Lq) return -1;
     const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
-    return min(item_cost(tile_range(s, i_lo, i_hi, p.g, causal != 0, bn)), kMaxBins - 1);
+    return min(tile_count(tile_range(s, i_lo, i_hi, p.g, p.win, causal != 0, bn)), kMaxBins - 1);
   };
   auto cost_of = [&](int idx) -> int { return idx < kCostCache ? (int)cost_cache[idx] : compute_cost(idx); };
   for (int base = 0; base < n_items; base += kPlanThreads) {  // uniform trip count: wave ops below
@@ -740,9 +754,9 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       }
     };
 
-    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
-    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
-    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, p.win, CAUSAL, BN);
+    const int n_tiles = tile_count(tr);
+    auto tile_at = [&](int n) { return nth_tile(tr, n); };
     // This chunk covers tiles [n_begin, n_end) of the item's tile sequence.
     const int n_begin = chunk * n_tiles / n_chunks, n_end = (chunk + 1) * n_tiles / n_chunks;
     const int n_steps = (n_end - n_begin + KSP - 1) / KSP;
@@ -769,6 +783,11 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     const int tlo_i = (p.g <= 0) ? s.H : (i >= s.H ? s.H + ((i - s.H) / p.g) * p.g : INT_MAX);
     const int a_i = CAUSAL ? min(hi_i, s.H - 1) : s.L - 1;
     const int b_i = CAUSAL ? max(tlo_i, s.H) : INT_MAX;
+    // Local window (p.win > 0, causal only): row i sees no key below
+    // i - win + 1, and a tile is full only if every row of the item sees its
+    // first key. Both are formed per tile from the kernel argument, so no
+    // register holds them across the loop.
+    const bool windowed = CAUSAL && p.win > 0;
 
 
     f32x16_t o[NDB];
@@ -855,7 +874,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // tile, so each variant below is straight-line code the scheduler can
       // interleave freely.
       const int j1 = min(j0 + BN, s.L);
-      const bool full = (j0 + BN <= s.L) &&
+      const bool full = (j0 + BN <= s.L) && (!windowed || j0 >= i_hi - p.win + 1) &&
                         (!CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc)));
 
       // K fragment (A operand of S^T) for key block jb, k step ks.
@@ -881,13 +900,15 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 
       // Visibility of the lane's keys in block jb as a bit mask over the
       // offset from its first key j = j0 + 32 jb + 4 half: bit o is set iff
-      // key j + o is visible, i.e. o <= a_i - j or b_i - j <= o <= i - j.
+      // key j + o is visible, i.e. o <= a_i - j or b_i - j <= o <= i - j,
+      // and o >= i - win + 1 - j (the local window).
       uint32_t vis[NJB];
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const int jbase = j0 + jb * 32 + 4 * half;
         const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
         vis[jb] = low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg));
+        if (windowed) vis[jb] &= ~low_bits(i - p.win + 1 - jbase);
       }
       f32x16_t sacc[NJB];
       V8 pf[NJB][2];
@@ -1341,9 +1362,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     };
 
-    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
-    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
-    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, p.win, CAUSAL, BN);
+    const int n_tiles = tile_count(tr);
+    auto tile_at = [&](int n) { return nth_tile(tr, n); };
     if (n_tiles > 0) dma_tile(tile_at(0), smem_k0, smem_v0);
 
     // Q fragments (B operand of S^T = K Q^T): lane (query l32, half) holds
@@ -1365,6 +1386,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int tlo_i = (p.g <= 0) ? s.H : (i >= s.H ? s.H + ((i - s.H) / p.g) * p.g : INT_MAX);
     const int a_i = CAUSAL ? min(hi_i, s.H - 1) : s.L - 1;
     const int b_i = CAUSAL ? max(tlo_i, s.H) : INT_MAX;
+    // Local window (p.win > 0, causal only): row i sees no key below
+    // i - win + 1, and a tile is full only if every row of the item sees its
+    // first key. Both are formed per tile from the kernel argument, so no
+    // register holds them across the loop.
+    const bool windowed = CAUSAL && p.win > 0;
 
     f32x16_t o[NDB];
 #pragma unroll
@@ -1386,7 +1412,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const char* vbuf = BUF == 0 ? smem_v0 : smem_v1;
       const int j0 = kt * BN;
       const int j1 = min(j0 + BN, s.L);
-      const bool full = (j0 + BN <= s.L) &&
+      const bool full = (j0 + BN <= s.L) && (!windowed || j0 >= i_hi - p.win + 1) &&
                         (!CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc)));
 
       // S^T = K Q^T: lane (key row, half) reads features 64 ks + 32 half .. + 31.
@@ -1415,6 +1441,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int jbase = j0 + jb * 32 + 4 * half;
         const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
         vis[jb] = full ? 0xffffffffu : (low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg)));
+        if (windowed && !full) vis[jb] &= ~low_bits(i - p.win + 1 - jbase);
       }
       auto pval = [&](int jb, int r) -> float {
         float sv = sacc[jb][r];
@@ -1592,11 +1619,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) v
     }
     const int hi_i = (i < s.nc) ? max(i, s.nc - 1) : i;
     const int tlo_i = (p.g <= 0) ? s.H : (i >= s.H ? s.H + ((i - s.H) / p.g) * p.g : INT_MAX);
-    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, CAUSAL, BN);
-    const int n_tiles = tr.ta + (tr.tb1 - tr.tb0);
+    // Local window: row i sees no key below w_i; every row of the item sees
+    // the keys from w_full on (both far below 0 without a window).
+    const int w_i = (CAUSAL && p.win > 0) ? i - p.win + 1 : -(1 << 30);
+    const int w_full = (CAUSAL && p.win > 0) ? i_hi - p.win + 1 : -(1 << 30);
+    const Tiles tr = tile_range(s, i_lo, i_hi, p.g, p.win, CAUSAL, BN);
+    const int n_tiles = tile_count(tr);
 
     f32x4_t kreg[PER_T], vreg[PER_T];
-    auto tile_at = [&](int n) { return n < tr.ta ? n : tr.tb0 + (n - tr.ta); };
+    auto tile_at = [&](int n) { return nth_tile(tr, n); };
     auto load_tile = [&](int kt) {
       const int j0 = kt * BN;
 #pragma unroll
@@ -1656,7 +1687,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) v
       }
 
       const int j1 = min(j0 + BN, s.L);
-      const bool full = !CAUSAL || ((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc));
+      const bool full = !CAUSAL || ((j0 >= w_full) &&
+                                    (((j1 - 1 <= i_lo) && (j1 <= s.H)) || ((i_hi < s.nc) && (j1 <= s.nc))));
       const float* rrow =
           RAB ? (const float*)p.rab + ((size_t)(b * p.rab_heads + (p.rab_heads == 1 ? 0 : h)) * p.max_seq_len + s.Lh +
                  q_loc) * p.max_seq_len
@@ -1671,7 +1703,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) v
           const float e = __builtin_amdgcn_exp2f(x * p.c_exp);
           float pv = x * __builtin_amdgcn_rcpf(1.f + e);
           if (CAUSAL && !full) {
-            const bool vis = (j < s.H) ? (j <= hi_i) : (j >= tlo_i && j <= i);
+            const bool vis = ((j < s.H) ? (j <= hi_i) : (j >= tlo_i && j <= i)) && (j >= w_i);
             pv = vis ? pv : 0.f;
           }
           sacc[jb][r] = pv;
@@ -1994,6 +2026,7 @@ KParams make_params(const FwdArgs& a) {
   while (a.paged && (1 << ps_log2) < a.page_size) ++ps_log2;
   p.ps_log2 = ps_log2;
   p.g = a.target_group_size;
+  p.win = a.causal ? a.local_window : 0;
   p.rab_vec = (a.max_seq_len % 4) == 0;
   p.alpha = a.alpha;
   // Both kernels evaluate 2^(c s) with c = -alpha*log2(e). The fp32 kernel

@@ -314,6 +314,19 @@ def fp8_gqa_causal(seed: int = 8, batch: int = 16) -> JaggedCase:
                        name="fp8_gqa_causal")
 
 
+def fp16_gqa_local(seed: int = 9, batch: int = 16) -> JaggedCase:
+    """The local mask on the GQA causal shape: as fp16_gqa_causal (batch 16,
+    lognormal lengths median 1500 clipped to [128, 4096], 8 query heads on 2
+    kv heads, d 128, fp16, num_targets ~ U{1..32}, group size 1, alpha
+    1/sqrt(128), out_scale 1/4096) with a local window of 512 positions (no
+    window size is given; 512 keeps a third of the median sequence)."""
+    rng = np.random.default_rng(seed)
+    lengths = np.clip(np.round(rng.lognormal(math.log(1500.0), 0.5, size=batch)), 128, 4096).astype(np.int64)
+    return jagged_case(seed + 1000, lengths, 8, 2, 128, "f16", mask_type=MASK_CAUSAL, num_targets=(1, 32),
+                       target_group_size=1, max_seq_len=4096, alpha=1.0 / math.sqrt(128), out_scale=1.0 / 4096,
+                       name="fp16_gqa_local", local_window=512)
+
+
 def bf16_paged_target(seed: int = 5, batch: int = 64) -> PagedCase:
     """64 requests, cached history ~ U{512..4096} in 64-token pages under a
     seeded shuffled block table, 1..64 new target tokens as queries
@@ -361,4 +374,5 @@ WORKLOADS: Dict[str, Callable[..., object]] = {
     "bf16_custom_mask": bf16_custom_mask,
     "bf16_delta_qk": bf16_delta_qk,
     "fp8_gqa_causal": fp8_gqa_causal,
+    "fp16_gqa_local": fp16_gqa_local,
 }

@@ -29,6 +29,11 @@
  * query i iff j <= i, or both i and j are context tokens (< nc). Key j >= H
  * (a target) is visible iff j <= i when g == 0; when g >= 1 only if i is a
  * target of the same group of g consecutive targets and j <= i.
+ * Local mask (feature table, local-mask row, which names the feature
+ * without defining it; read here as a sliding window): with local_window
+ * W >= 1, key j is visible to query i only if the causal mask above allows
+ * it and i - j < W. The window bounds every pair alike (context, history and
+ * targets); W = 0 means no window. It is taken with HSTU_MASK_CAUSAL only.
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE memory owned by the caller. The library
@@ -132,15 +137,17 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
  *  num_context, num_targets [batch] int32, or NULL (= all zero). Must be
  *                NULL unless mask_type is HSTU_MASK_CAUSAL.
  *  target_group_size >= 0 (0 = no target mask).
+ *  local_window  >= 0: the local mask's window W (0 = none); nonzero only
+ *                with HSTU_MASK_CAUSAL.
  *  alpha         scale applied to (Q.K^T + rab) before SiLU.
  *  out_scale     scale applied after SiLU (the page's silu_scale; its default
  *                is 1/max_seq_len, applied by the Python binding).
  * Errors: HSTU_ERR_INVALID_ARG for negative sizes, num_heads_q not a
  * multiple of num_heads_kv, null q/k/v/out/seq_offsets, pointers not 16-byte
- * aligned, num_context/num_targets with a mask other than causal, a mask
- * without HSTU_MASK_CUSTOM or HSTU_MASK_CUSTOM without a mask, rab or mask
- * head counts other than 1 and num_heads_q, target_group_size < 0 or an
- * unknown mask code; HSTU_ERR_UNSUPPORTED for mask code 1, head_dim, dtype,
+ * aligned, num_context/num_targets or local_window > 0 with a mask other
+ * than causal, a mask without HSTU_MASK_CUSTOM or HSTU_MASK_CUSTOM without a
+ * mask, rab or mask head counts other than 1 and num_heads_q,
+ * target_group_size < 0, local_window < 0 or an unknown mask code; HSTU_ERR_UNSUPPORTED for mask code 1, head_dim, dtype,
  * HSTU_MASK_CUSTOM in f32, or HSTU_FP8_E4M3 with rab, the user mask or
  * seq_offsets_k; HSTU_ERR_WORKSPACE if workspace_bytes is too small;
  * HSTU_ERR_HIP if a launch fails.
@@ -149,8 +156,9 @@ hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* 
                        const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
                        const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
                        int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
-                       hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
-                       hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+                       hstu_mask_t mask_type, int32_t target_group_size, int32_t local_window, float alpha,
+                       float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       void* stream /* hipStream_t */);
 
 /*
  * hstu_fwd in two steps, for callers that time or reuse them separately
@@ -167,22 +175,25 @@ hstu_status_t hstu_fwd(const void* q, const void* k, const void* v, const void* 
  * hstu_fwd_run: the fused forward kernel alone, consuming the plan held in
  * `workspace`. The caller guarantees that the plan was made with the same
  * seq_offsets / seq_offsets_k contents, num_context, num_targets, batch,
- * max_seq_len, head counts, head_dim, mask_type, target_group_size and
- * dtype, and that no other call uses the workspace between the plan and the
- * run. A run leaves the plan intact, so further runs may follow.
+ * max_seq_len, head counts, head_dim, mask_type, target_group_size,
+ * local_window and dtype, and that no other call uses the workspace between
+ * the plan and the run. A run leaves the plan intact, so further runs may
+ * follow.
  * hstu_fwd == plan + run.
  */
 hstu_status_t hstu_fwd_plan(const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
                             const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
                             int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type, int32_t target_group_size,
-                            hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+                            int32_t local_window, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                            void* stream /* hipStream_t */);
 
 hstu_status_t hstu_fwd_run(const void* q, const void* k, const void* v, const void* rab, const void* mask, void* out,
                            const int32_t* seq_offsets, const int32_t* seq_offsets_k, const int32_t* num_context,
                            const int32_t* num_targets, int32_t batch, int32_t max_seq_len, int32_t num_heads_q,
                            int32_t num_heads_kv, int32_t head_dim, int32_t rab_num_heads, int32_t mask_num_heads,
-                           hstu_mask_t mask_type, int32_t target_group_size, float alpha, float out_scale,
-                           hstu_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+                           hstu_mask_t mask_type, int32_t target_group_size, int32_t local_window, float alpha,
+                           float out_scale, hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                           void* stream /* hipStream_t */);
 
 /*
  * Workspace bytes hstu_fwd_paged needs. max_seq_len bounds history + new
@@ -215,8 +226,9 @@ hstu_status_t hstu_fwd_paged(const void* q, const void* k_new, const void* v_new
                              const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
                              const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                             int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
-                             void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+                             int32_t target_group_size, int32_t local_window, float alpha, float out_scale,
+                             hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             void* stream /* hipStream_t */);
 
 /* hstu_fwd_paged in two steps, with the same contract as hstu_fwd_plan /
  * hstu_fwd_run. The plan reads seq_offsets_q, page_offsets, last_page_len,
@@ -226,7 +238,7 @@ hstu_status_t hstu_fwd_paged_plan(const int32_t* seq_offsets_q, const int32_t* p
                                   const int32_t* last_page_len, const int32_t* num_context, const int32_t* num_targets,
                                   int32_t batch, int32_t page_size, int32_t max_seq_len, int32_t num_heads_q,
                                   int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                                  int32_t target_group_size, hstu_dtype_t dtype, void* workspace,
+                                  int32_t target_group_size, int32_t local_window, hstu_dtype_t dtype, void* workspace,
                                   size_t workspace_bytes, void* stream /* hipStream_t */);
 
 hstu_status_t hstu_fwd_paged_run(const void* q, const void* k_new, const void* v_new, void* out,
@@ -234,8 +246,9 @@ hstu_status_t hstu_fwd_paged_run(const void* q, const void* k_new, const void* v
                                  const int32_t* page_ids, const int32_t* last_page_len, const int32_t* num_context,
                                  const int32_t* num_targets, int32_t batch, int32_t page_size, int32_t max_seq_len,
                                  int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim, hstu_mask_t mask_type,
-                                 int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
-                                 void* workspace, size_t workspace_bytes, void* stream /* hipStream_t */);
+                                 int32_t target_group_size, int32_t local_window, float alpha, float out_scale,
+                                 hstu_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream /* hipStream_t */);
 
 /*
  * hstu_fwd without a workspace argument, for callers that cannot allocate
@@ -258,8 +271,8 @@ hstu_status_t hstu_fwd_noalloc(const void* q, const void* k, const void* v, cons
                                const int32_t* num_context, const int32_t* num_targets, int32_t batch,
                                int32_t max_seq_len, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                                int32_t rab_num_heads, int32_t mask_num_heads, hstu_mask_t mask_type,
-                               int32_t target_group_size, float alpha, float out_scale, hstu_dtype_t dtype,
-                               void* stream /* hipStream_t */);
+                               int32_t target_group_size, int32_t local_window, float alpha, float out_scale,
+                               hstu_dtype_t dtype, void* stream /* hipStream_t */);
 
 /* Static description of a status code. Never NULL. */
 const char* hstu_status_string(hstu_status_t status);

@@ -4,6 +4,7 @@ from __future__ import annotations
 
 import numpy as np
 import torch
+from scipy.special import expit
 
 import hstu_jagged_attention_amd as hj
 import oracle
@@ -97,6 +98,65 @@ def oracle_paged(pc, rows=None) -> np.ndarray:
                                  num_targets=pc.num_targets, mask_type=pc.mask_type,
                                  target_group_size=pc.target_group_size, alpha=pc.alpha, out_scale=pc.out_scale,
                                  rows=rows, local_window=pc.local_window)
+
+
+def fp8_cast_allowance(c, toks, heads, eps=2.0 ** -14):
+    """Both roundings of an E4M3 cast of P are valid where P lies within a
+    relative eps of a rounding midpoint: the kernel computes P in fp32 with
+    the hardware exp2 / reciprocal (a few ulp), the oracle in float64, and
+    the two can fall on either side. eps = 2^-14 is far above fp32's
+    rounding (2^-24) and far below an E4M3 step (2^-4 relative at least).
+    For the (token, head) pairs given, returns the largest change of O
+    those casts can make: out_scale * sum over such keys of (the gap between
+    the two candidate E4M3 values) * |V[j, :]|, shape [n, D]."""
+    import oracle
+    q, k, v = f64(c.q), f64(c.k), f64(c.v)
+    koff = c.seq_offsets if c.seq_offsets_k is None else c.seq_offsets_k
+    Hq, Hk = q.shape[1], k.shape[1]
+    toks, heads = np.asarray(toks), np.asarray(heads)
+    out = np.zeros((len(toks), q.shape[2]))
+    cast = lambda x: torch.from_numpy(np.minimum(x, 448.0)).float().to(torch.float8_e4m3fn).double().numpy()
+    b_of = np.searchsorted(c.seq_offsets, toks, side="right") - 1
+    for b in np.unique(b_of):
+        s0, s1, k0, k1 = int(c.seq_offsets[b]), int(c.seq_offsets[b + 1]), int(koff[b]), int(koff[b + 1])
+        Lk = k1 - k0
+        nc = 0 if c.num_context is None else int(c.num_context[b])
+        nt = 0 if c.num_targets is None else int(c.num_targets[b])
+        M = oracle.mask_matrix(c.mask_type, Lk, nc, nt, c.target_group_size, c.local_window)
+        for h in np.unique(heads[b_of == b]):
+            sel = np.nonzero((b_of == b) & (heads == h))[0]
+            hk = int(h) * Hk // Hq
+            pos = (Lk - (s1 - s0)) + toks[sel] - s0  # key positions of the queries
+            a = c.alpha * (q[toks[sel], h, :] @ k[k0:k1, hk, :].T)
+            p = a * expit(a)
+            gap = np.where(M[pos], np.abs(cast(p * (1 + eps)) - cast(p * (1 - eps))), 0.0)
+            out[sel] = c.out_scale * (gap @ np.abs(v[k0:k1, hk, :]))
+    return out
+
+
+def assert_parity_fp8(got, ref, c, toks=None, heads=None, what: str = ""):
+    """The FP8 cast's comparison: the bars of the other 16-bit dtypes on the
+    raw difference (max-abs, relative L2), and the relative max-abs bar on
+    what remains after the cast-midpoint allowance of each element (see
+    fp8_cast_allowance). toks / heads: the (token, head) of each row of
+    got / ref ([n, D]); default, every row of a [T, H, D] output."""
+    g, r = f64(got), np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    if toks is None:
+        T, H = g.shape[0], g.shape[1]
+        toks, heads = np.repeat(np.arange(T), H), np.tile(np.arange(H), T)
+        g, r = g.reshape(T * H, -1), r.reshape(T * H, -1)
+    max_abs, rel_l2, ref_max = errors(g, r)
+    t = TOL["fp8"]
+    allow = fp8_cast_allowance(c, np.asarray(toks), np.asarray(heads))
+    excess = float(np.max(np.abs(g - r) - allow, initial=0.0))
+    msg = (f"{what}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} max|ref|={ref_max:.3e} "
+           f"beyond cast allowance={excess:.3e} (rows with an ambiguous cast: {int((allow > 0).any(1).sum())})")
+    assert max_abs <= t["max_abs"], msg
+    assert rel_l2 <= t["rel_l2"], msg
+    assert excess <= t["rel_max"] * max(ref_max, 1e-30), msg
+    return max_abs, rel_l2
 
 
 def errors(got, ref):

@@ -48,22 +48,22 @@ def test_status_strings(lib):
 
 def fwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, rab=None, umask=None, out=FAKE, off=FAKE, offk=None, nc=None, nt=None, B=2,
-             S=128, Hq=4, Hk=2, D=128, rab_h=4, mask_h=4, mask=0, g=0, alpha=1.0, osc=1.0, dt=BF16, ws=FAKE,
-             wsb=1 << 30, stream=None)
+             S=128, Hq=4, Hk=2, D=128, rab_h=4, mask_h=4, mask=0, g=0, win=0, alpha=1.0, osc=1.0, dt=BF16,
+             ws=FAKE, wsb=1 << 30, stream=None)
     a.update(kw)
     return lib.hstu_fwd(a["q"], a["k"], a["v"], a["rab"], a["umask"], a["out"], a["off"], a["offk"], a["nc"],
                         a["nt"], a["B"], a["S"], a["Hq"], a["Hk"], a["D"], a["rab_h"], a["mask_h"], a["mask"], a["g"],
-                        a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"], a["stream"])
+                        a["win"], a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 def paged(lib, **kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, out=FAKE, offq=FAKE, cache=FAKE, poff=FAKE, pids=FAKE, lpl=FAKE, nc=None,
-             nt=None, B=2, ps=64, S=128, Hq=4, Hk=4, D=128, mask=0, g=1, alpha=1.0, osc=1.0, dt=BF16, ws=FAKE,
-             wsb=1 << 20, stream=None)
+             nt=None, B=2, ps=64, S=128, Hq=4, Hk=4, D=128, mask=0, g=1, win=0, alpha=1.0, osc=1.0, dt=BF16,
+             ws=FAKE, wsb=1 << 20, stream=None)
     a.update(kw)
     return lib.hstu_fwd_paged(a["q"], a["kn"], a["vn"], a["out"], a["offq"], a["cache"], a["poff"], a["pids"],
                               a["lpl"], a["nc"], a["nt"], a["B"], a["ps"], a["S"], a["Hq"], a["Hk"], a["D"], a["mask"],
-                              a["g"], a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"], a["stream"])
+                              a["g"], a["win"], a["alpha"], a["osc"], a["dt"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_empty_inputs_are_a_noop(lib):
@@ -111,6 +111,10 @@ def test_empty_inputs_are_a_noop(lib):
     (dict(dt=FP8, mask=3, umask=FAKE), UNSUP),  # ... or the user mask
     (dict(dt=FP8, offk=FAKE), UNSUP),         # ... or separate key offsets
     (dict(dt=4), UNSUP),
+    (dict(win=-1), INVAL),                    # negative local window
+    (dict(win=-1, B=0), INVAL),               # ... even for an empty input
+    (dict(win=8, mask=2), INVAL),             # the local window needs the causal mask
+    (dict(win=8, mask=3, umask=FAKE), INVAL),
 ])
 def test_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -128,6 +132,8 @@ def test_fwd_rejects(lib, kw, code):
     (dict(wsb=8), WS),
     (dict(B=2049), INVAL),
     (dict(dt=FP8), UNSUP),                    # the FP8 cast is built for jagged calls
+    (dict(win=-3), INVAL),
+    (dict(win=16, mask=2), INVAL),
 ])
 def test_paged_rejects(lib, kw, code):
     assert paged(lib, **kw) == code

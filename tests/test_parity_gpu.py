@@ -11,8 +11,8 @@ import torch
 
 import hstu_jagged_attention_amd as hj
 from hstu_jagged_attention_amd import workloads as wl
-from _helpers import (assert_parity, f64, gpu_device, oracle_jagged, oracle_jagged_sampled, oracle_paged, run_jagged,
-                      run_paged)
+from _helpers import (assert_parity, assert_parity_fp8, f64, gpu_device, oracle_jagged, oracle_jagged_sampled,
+                      oracle_paged, run_jagged, run_paged)
 
 pytestmark = pytest.mark.gpu
 CAUSAL, NONE = wl.MASK_CAUSAL, wl.MASK_NONE
@@ -270,7 +270,7 @@ def test_fp8_cast(dev, case):
     say(name, "batch", c.batch, "heads", Hq, Hk)
     got = run_jagged(c, dev)
     assert got.dtype == torch.bfloat16
-    _, rel_cast = assert_parity(got, oracle_jagged(c), "fp8", name)
+    _, rel_cast = assert_parity_fp8(got, oracle_jagged(c), c, what=name)
     import oracle as orc
     plain = orc.hstu_fwd(f64(c.q), f64(c.k), f64(c.v), c.seq_offsets, num_context=c.num_context,
                          num_targets=c.num_targets, max_seq_len=c.max_seq_len, mask_type=c.mask_type,
@@ -283,13 +283,14 @@ def test_fp8_cast(dev, case):
 def test_fp8_workload_reduced_and_sampled(dev):
     c = wl.fp8_gqa_causal(batch=2)
     say("fp8_gqa_causal batch 2", c.lengths.tolist())
-    assert_parity(run_jagged(c, dev), oracle_jagged(c), "fp8", "fp8_gqa_causal reduced")
+    assert_parity_fp8(run_jagged(c, dev), oracle_jagged(c), c, what="fp8_gqa_causal reduced")
     c = wl.fp8_gqa_causal()
     say("fp8_gqa_causal full size: B", c.batch, "T", int(c.seq_offsets[-1]))
     got = run_jagged(c, dev).cpu()
     ref = oracle_jagged_sampled(c, _picks(c))
     for b, (toks, heads, vals) in ref.items():
-        assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, "fp8", f"fp8_gqa_causal seq {b}")
+        assert_parity_fp8(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, c, toks, heads,
+                          f"fp8_gqa_causal seq {b}")
 
 
 def test_every_row_is_written(dev):
@@ -576,7 +577,7 @@ def _raw_fwd(c, dev, off, max_seq_len, offk=None, out=None):
     P = ctypes.c_void_p
     st = lib.hstu_fwd(P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), None, None, P(out.data_ptr()),
                       P(offd.data_ptr()), None if offkd is None else P(offkd.data_ptr()), None, None, B, max_seq_len,
-                      Hq, Hk, D, 1, 1, CAUSAL, 0, c.alpha, c.out_scale, code, P(ws.data_ptr()), need,
+                      Hq, Hk, D, 1, 1, CAUSAL, 0, 0, c.alpha, c.out_scale, code, P(ws.data_ptr()), need,
                       P(torch.cuda.current_stream(dev).cuda_stream))
     torch.cuda.synchronize(dev)
     return st, out
@@ -655,7 +656,10 @@ def test_guard_bands_stay_intact(dev, kind):
         obuf, ob = _guarded(c.q.shape[0] * c.q.shape[1] * c.q.shape[2] * 2, dev, 0x5A)
         out = ob.view(odt).view(tuple(c.q.shape))
         got = run_jagged(c, dev, out=out, workspace=ws)
-        assert_parity(got, oracle_jagged(c), c.dtype, f"guarded {kind}")
+        if c.dtype == "fp8":
+            assert_parity_fp8(got, oracle_jagged(c), c, what=f"guarded {kind}")
+        else:
+            assert_parity(got, oracle_jagged(c), c.dtype, f"guarded {kind}")
     torch.cuda.synchronize(dev)
     for buf, fill, what in ((wbuf, 0xA5, "workspace"), (obuf, 0x5A, "out")):
         head, tail = buf[:GUARD], buf[-GUARD:]
@@ -678,3 +682,65 @@ def test_paged_block_table_permutation_bit_identical(dev):
     pc.page_ids = perm[pc.page_ids]
     b = run_paged(pc, dev)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ local mask (sliding window on the causal mask)
+LOCAL_MIX = [int(x) for x in np.resize([0, 1, 2, 31, 33, 63, 64, 65, 127, 129, 200, 256, 257, 300, 511, 700], 64)]
+LOCAL = [
+    # (name, key lengths, query lengths or None, Hq, Hk, D, dtype, nc, nt, g, rab_std, W)
+    ("w1_bf16_direct", [200, 77, 300, 1], None, 4, 4, 128, "bf16", None, None, 0, None, 1),
+    ("w64_f16_gqa_ctx_targets", [150, 270, 33], None, 8, 2, 128, "f16", (0, 20), (1, 40), 1, None, 64),
+    ("w65_bf16_d64_ctx", [300, 129, 64], None, 2, 2, 64, "bf16", (0, 90), None, 0, None, 65),
+    ("w100_bf16_rab_work_list", LOCAL_MIX, None, 2, 2, 128, "bf16", (0, 12), (0, 40), 1, 0.5, 100),
+    ("w37_f16_d64_targets_g3_work_list", LOCAL_MIX, None, 8, 2, 64, "f16", None, (1, 90), 3, None, 37),
+    ("w300_f16_gqa4_work_list", LOCAL_MIX, None, 8, 2, 128, "f16", None, (1, 32), 1, None, 300),
+    ("w_ge_length_bf16", [200, 300], None, 2, 2, 128, "bf16", None, (0, 9), 1, None, 5000),
+    ("w200_d256_bf16_rab", [300, 129], None, 2, 2, 256, "bf16", None, (1, 30), 1, 0.1, 200),
+    ("w7_d32_f16_ctx", [0, 40, 1, 130], None, 2, 2, 32, "f16", (0, 5), None, 0, None, 7),
+    ("w33_f32_rab", [200, 90], None, 2, 2, 64, "f32", None, (1, 20), 1, 0.5, 33),
+    ("w129_delta_split", [600, 333, 1030], [40, 333, 1], 4, 4, 128, "bf16", None, [40, 333, 1], 1, None, 129),
+    ("w64_delta_many", [500 + 13 * i for i in range(48)], [1 + (5 * i) % 64 for i in range(48)], 4, 4, 128, "bf16",
+     None, [1 + (5 * i) % 64 for i in range(48)], 1, None, 64),
+    ("w65_fp8_gqa_ctx_targets", [150, 270, 33], None, 8, 2, 128, "fp8", (0, 20), (1, 40), 1, None, 65),
+    ("w100_fp8_work_list_g3", LOCAL_MIX, None, 4, 2, 128, "fp8", (0, 12), (1, 50), 3, None, 100),
+]
+
+
+@pytest.mark.parametrize("case", LOCAL, ids=[e[0] for e in LOCAL])
+def test_local_window(dev, case):
+    """The local mask (key j visible to query i only when the causal mask
+    allows it and i - j < W), element by element against the oracle: windows
+    of 1 to beyond the sequence, context and targets, GQA, head dims 32..256,
+    every dtype, the direct and work-list modes and key-split delta-QK."""
+    name, lk, lq, Hq, Hk, D, dt, nc, nt, g, rab_std, W = case
+    seed = zlib.crc32(name.encode()) & 0xffff
+    say(name, "seed", seed, "window", W, "batch", len(lk))
+    c = wl.jagged_case(seed, lk, Hq, Hk, D, dt, mask_type=CAUSAL, num_context=nc, num_targets=nt,
+                       target_group_size=g, rab_std=rab_std, q_lengths=lq, name=name, local_window=W)
+    got = run_jagged(c, dev)
+    if dt == "fp8":
+        assert_parity_fp8(got, oracle_jagged(c), c, what=name)
+    else:
+        assert_parity(got, oracle_jagged(c), dt, name)
+    if W >= int(c.key_lengths.max(initial=0)):
+        # a window covering every sequence is no window, bit for bit
+        assert torch.equal(got, run_jagged(c, dev, local_window=0))
+
+
+def test_local_window_paged(dev):
+    pc = wl.paged_case(57, [0, 1, 63, 64, 65, 300, 1000], [3, 1, 7, 64, 2, 33, 40], 4, 2, 128, "bf16", page_size=64,
+                       num_context=(0, 4), target_group_size=1, extra_pages=2, local_window=70)
+    say("paged local window 70")
+    assert_parity(run_paged(pc, dev), oracle_paged(pc), "bf16", "paged local window")
+
+
+def test_local_window_workload_reduced_and_sampled(dev):
+    c = wl.fp16_gqa_local(batch=2)
+    say("fp16_gqa_local batch 2", c.lengths.tolist())
+    assert_parity(run_jagged(c, dev), oracle_jagged(c), "f16", "fp16_gqa_local reduced")
+    c = wl.fp16_gqa_local()
+    say("fp16_gqa_local full size: B", c.batch, "T", int(c.seq_offsets[-1]))
+    got = run_jagged(c, dev).cpu()
+    ref = oracle_jagged_sampled(c, _picks(c))
+    for b, (toks, heads, vals) in ref.items():
+        assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, "f16", f"fp16_gqa_local seq {b}")

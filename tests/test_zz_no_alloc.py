@@ -22,7 +22,8 @@ def _noalloc(c, dev):
     kw = dict(rab=None if c.rab is None else c.rab.to(dev), mask=None if c.mask is None else c.mask.to(dev),
               seq_offsets_k=None if c.seq_offsets_k is None else torch.as_tensor(c.seq_offsets_k),
               num_context=c.num_context, num_targets=c.num_targets, max_seq_len=c.max_seq_len,
-              mask_type=c.mask_type, target_group_size=c.target_group_size, alpha=c.alpha, out_scale=c.out_scale)
+              mask_type=c.mask_type, target_group_size=c.target_group_size, local_window=c.local_window,
+              alpha=c.alpha, out_scale=c.out_scale)
     return hj.hstu_fwd_noalloc(c.q.to(dev), c.k.to(dev), c.v.to(dev), torch.as_tensor(c.seq_offsets), out=out, **kw)
 
 
@@ -32,7 +33,7 @@ def test_noalloc_matches_hstu_fwd_twice_second_smaller():
                          num_context=(0, 12), num_targets=(0, 40), target_group_size=1, rab_std=0.3, max_seq_len=300,
                          name="noalloc_big")
     small = wl.jagged_case(502, [70, 1, 130], 4, 4, 64, "bf16", num_targets=(1, 9), target_group_size=2,
-                           max_seq_len=130, name="noalloc_small")
+                           max_seq_len=130, name="noalloc_small", local_window=50)
     for c in (big, small):
         print("[case]", c.name, "batch", c.batch, flush=True)
         ref = run_jagged(c, dev)
