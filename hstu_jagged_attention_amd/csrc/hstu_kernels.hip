@@ -902,14 +902,17 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // offset from its first key j = j0 + 32 jb + 4 half: bit o is set iff
       // key j + o is visible, i.e. o <= a_i - j or b_i - j <= o <= i - j,
       // and o >= i - win + 1 - j (the local window).
+      // Built on masked tiles only (full tiles never read it).
       uint32_t vis[NJB];
+      auto make_vis = [&]() {
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const int jbase = j0 + jb * 32 + 4 * half;
-        const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
-        vis[jb] = low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg));
-        if (windowed) vis[jb] &= ~low_bits(i - p.win + 1 - jbase);
-      }
+        for (int jb = 0; jb < NJB; ++jb) {
+          const int jbase = j0 + jb * 32 + 4 * half;
+          const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
+          vis[jb] = low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg));
+          if (windowed) vis[jb] &= ~low_bits(i - p.win + 1 - jbase);
+        }
+      };
       f32x16_t sacc[NJB];
       V8 pf[NJB][2];
       // S block jb times y_mul (only when Q was scaled by c / y_mul).
@@ -1043,10 +1046,12 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int jb = 1; jb < NJB; ++jb) pv_block(jb, false);
         };
-        if (full)
+        if (full) {
           body(std::false_type{});
-        else
+        } else {
+          make_vis();
           body(std::true_type{});
+        }
       } else {
         // Two waves per SIMD: the other wave on the SIMD fills the gaps of
         // this one. The body is cut into small scheduling regions (by
@@ -1099,10 +1104,12 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int jb = 0; jb < NJB; ++jb) epi_block(masked, jb);
         };
-        if (full)
+        if (full) {
           epi_all(std::false_type{});
-        else
+        } else {
+          make_vis();
           epi_all(std::true_type{});
+        }
 #pragma unroll
         for (int g = 0; g < NGP; ++g) {
           if (g + 1 < NGP) {
