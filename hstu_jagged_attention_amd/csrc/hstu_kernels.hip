@@ -25,7 +25,10 @@
 //     rows for MHA, up to 4 heads x 32 rows for GQA), so each K/V tile is
 //     staged through LDS once for all of them. K/V tiles go global -> LDS by
 //     DMA (no register staging), double buffered, into rows padded so every
-//     fragment read is conflict-free. Per key tile: S^T = K Q^T on MFMA (the
+//     fragment read is conflict-free. rab and the user mask go through a
+//     ring of three LDS tiles by DMA, two tiles ahead, where LDS allows and
+//     max_seq_len is a multiple of 8 (else into registers, one tile ahead).
+//     Per key tile: S^T = K Q^T on MFMA (the
 //     accumulator then holds one query per lane and 16 keys per lane), the
 //     SiLU epilogue in registers, then O^T += V^T P^T on MFMA with P used
 //     straight from the S^T registers as the B operand; the V^T A operand
@@ -572,7 +575,11 @@ __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  
 // for work lists too short to fill the chip.
 // MSK: the user mask (mask_type 3, no built-in mask): its value m for
 // (i, j) multiplies P, and m == 0 removes the key like the built-in masks do.
-template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE, int KSP, bool MSK = false>
+// SQL: which of rab (bit 0) and the user mask (bit 1) are staged through a
+// ring of three LDS tiles by DMA, two tiles ahead (the others are loaded
+// into registers one tile ahead). Needs KSP == 1 and rows of max_seq_len
+// elements that are 16-byte multiples.
+template <typename T, int D, int BN, bool CAUSAL, bool RAB, bool PAGED, int WPE, int KSP, bool MSK = false, int SQL = 0>
 __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(WPE))) void fwd_kernel(KParams p) {
   using F = Frag<T>;
   using V8 = typename F::v8;
@@ -594,6 +601,20 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
   constexpr int K_BLK = K_TILE_B / 1024, V_BLK = V_TILE_B / 1024;
   constexpr int K_BLK_W = (K_BLK + kWaves - 1) / kWaves, V_BLK_W = (V_BLK + kWaves - 1) / kWaves;
   static_assert(KSP == 1 || (KSP == 2 && BN == 64), "the key split exchanges O through one 64-key K/V buffer per wave");
+  // Side-tensor ring (see SQL): one tile of one tensor holds the BN keys of
+  // the 128 (query row, head) pairs of the item, row r of the tile (pair
+  // r = 32 w + l of wave w, lane l) in BN * 2 bytes whose 16-byte chunks
+  // are permuted by the swizzle below, so that the 8-byte reads of the 32
+  // rows of a wave spread over all banks.
+  constexpr bool R_LDS = RAB && (SQL & 1), M_LDS = MSK && (SQL & 2);
+  constexpr int N_RING = (R_LDS ? 1 : 0) + (M_LDS ? 1 : 0);
+  constexpr int RING = 3;
+  constexpr int SQ_ROW_B = BN * 2;
+  constexpr int SQ_TILE_B = kWaves * kRowsPerWave * SQ_ROW_B;
+  constexpr int SQ_CH = SQ_ROW_B / 16;         // 16-byte chunks per row
+  constexpr int SQ_G = 256 / SQ_ROW_B;         // rows per sweep of the 64 banks
+  constexpr int SQ_BLK_W = SQ_TILE_B / 1024 / kWaves;  // DMA blocks per wave per tile
+  static_assert(N_RING == 0 || (KSP == 1 && SQ_TILE_B % (1024 * kWaves) == 0 && SQ_G >= 1), "side-tensor ring");
   using Buf0 = std::integral_constant<int, 0>;
   using Buf1 = std::integral_constant<int, 1>;
 
@@ -605,6 +626,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(1024))) char smem_v0[KSP][V_TILE_B];
   __shared__ __attribute__((aligned(1024))) char smem_k1[KSP][K_TILE_B];
   __shared__ __attribute__((aligned(1024))) char smem_v1[KSP][V_TILE_B];
+  __shared__ __attribute__((aligned(1024))) char smem_sq[N_RING ? N_RING * RING : 1][N_RING ? SQ_TILE_B : 16];
   __shared__ int sh_item[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -805,6 +827,47 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     };
     const T* rrow = RAB ? sq_row(p.rab, p.rab_heads) : nullptr;
     const T* mrow = MSK ? sq_row(p.mask, p.mask_heads) : nullptr;
+    // Ring DMA geometry of this lane: in block u it fills 16-byte slot
+    // (blk * 64 + lane) of a tile, blk = wave + kWaves u, i.e. chunk cp of
+    // row P, holding the 8 keys of chunk cp ^ swizzle(P) of pair P. Rows
+    // past the sequence repeat its last row; chunks past max_seq_len repeat
+    // the row's last chunk (those keys are masked).
+    const T* ring_row[N_RING ? N_RING : 1][N_RING ? SQ_BLK_W : 1];
+    int ring_col[N_RING ? SQ_BLK_W : 1];
+    if constexpr (N_RING > 0) {
+#pragma unroll
+      for (int u = 0; u < SQ_BLK_W; ++u) {
+        const int slot = (wave + kWaves * u) * 64 + lane;
+        const int P = slot / SQ_CH, cp = slot % SQ_CH;
+        ring_col[u] = 8 * (cp ^ ((P / SQ_G) % SQ_CH));
+        const int w = P / kRowsPerWave;
+        const int hh = hg * hpw + (w & (hpw - 1));
+        const int qq = q_lo + (w >> p.hpw_log2) * kRowsPerWave + P % kRowsPerWave;
+        const int row = s.Lh + min(qq, max(s.Lq - 1, 0));
+        int t = 0;
+        if constexpr (R_LDS)
+          ring_row[t++][u] = (const T*)p.rab + ((size_t)(b * p.rab_heads + (p.rab_heads == 1 ? 0 : hh)) * p.max_seq_len + row) * p.max_seq_len;
+        if constexpr (M_LDS)
+          ring_row[t++][u] = (const T*)p.mask + ((size_t)(b * p.mask_heads + (p.mask_heads == 1 ? 0 : hh)) * p.max_seq_len + row) * p.max_seq_len;
+      }
+    }
+    // DMA of the side tensors' tile n (of the chunk) into ring slot rs.
+    auto ring_dma = [&](int n, int rs) {
+      if constexpr (N_RING > 0) {
+        const int j0 = tile_at(n) * BN;
+#pragma unroll
+        for (int t = 0; t < N_RING; ++t)
+#pragma unroll
+          for (int u = 0; u < SQ_BLK_W; ++u)
+            dma16(ring_row[t][u] + min(j0 + ring_col[u], p.max_seq_len - 8),
+                  smem_sq[t * RING + rs] + (wave + kWaves * u) * 1024);
+      }
+    };
+    // This lane's rab / mask words of ring slot rs, in the register layout
+    // of the prefetch below.
+    const int ring_pair = wave * kRowsPerWave + l32;
+    const int ring_off = ring_pair * SQ_ROW_B + 8 * half;
+    const int ring_swz = (ring_pair / SQ_G) % SQ_CH;
     // rab (or mask) of the tile at key j0: lane holds row q_loc, keys
     // j0 + 32 jb + 8 a + 4 half + 0..3. Loaded one step ahead (issued right
     // after the next tile's DMA), so the step that uses it never waits for
@@ -831,8 +894,16 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     };
     RabRegs rv_next, mv_next;
     if (n_begin + GRP < n_end) {
-      if constexpr (RAB) load_rab(rrow, tile_at(n_begin + GRP) * BN, rv_next);
-      if constexpr (MSK) load_rab(mrow, tile_at(n_begin + GRP) * BN, mv_next);
+      if constexpr (RAB && !R_LDS) load_rab(rrow, tile_at(n_begin + GRP) * BN, rv_next);
+      if constexpr (MSK && !M_LDS) load_rab(mrow, tile_at(n_begin + GRP) * BN, mv_next);
+    }
+    // The ring's first two tiles, after every other load of the prologue:
+    // the first step then waits for all but the second.
+    int ring_slot = 0;
+    if constexpr (N_RING > 0) {
+      asm volatile("" ::: "memory");
+      ring_dma(n_begin, 0);
+      if (n_begin + 1 < n_end) ring_dma(n_begin + 1, 1);
     }
     const int G = lane >> 4, sl = lane & 15;
 
@@ -843,29 +914,62 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       const int n = n_begin + KSP * t + GRP;
       const bool has_tile = n < n_end;
       const int kt = tile_at(has_tile ? n : n_begin);
-      wait_vmem_all();
+      const int cur = ring_slot;  // ring slot of this tile
+      ring_slot = cur == RING - 1 ? 0 : cur + 1;
+      if constexpr (N_RING > 0) {
+        // This tile's K/V DMA and ring tile must have landed; the ring DMA
+        // issued last after them (tile n + 1, when it exists) may stay in
+        // flight. The ring DMAs are the last vector memory instructions a
+        // step issues.
+        constexpr int NRD = N_RING * SQ_BLK_W;
+        static_assert(NRD < 16, "vmcnt field");
+        if (n + 1 < n_end)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | NRD);  // vmcnt(NRD)
+        else
+          wait_vmem_all();
+      } else {
+        wait_vmem_all();
+      }
       __syncthreads();
       const int j0 = kt * BN;
 
       // The next tile's DMA goes out first: it has a whole step to land;
-      // then the next tile's rab (this tile's arrived last step).
+      // then the next tile's rab (this tile's arrived last step), then the
+      // ring tile two ahead, into the slot the last step read.
       if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
       RabRegs rv, mv;
-      if constexpr (RAB) {
+      if constexpr (RAB && !R_LDS) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int a = 0; a < 4; ++a) rv[jb][a] = rv_next[jb][a];
         if (n + KSP < n_end) load_rab(rrow, tile_at(n + KSP) * BN, rv_next);
       }
-      if constexpr (MSK) {
+      if constexpr (MSK && !M_LDS) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
           for (int a = 0; a < 4; ++a) mv[jb][a] = mv_next[jb][a];
         if (n + KSP < n_end) load_rab(mrow, tile_at(n + KSP) * BN, mv_next);
       }
+      if constexpr (N_RING > 0) {
+        asm volatile("" ::: "memory");
+        if (n + 2 < n_end) ring_dma(n + 2, cur == 0 ? RING - 1 : cur - 1);
+      }
       if (!wave_active || !has_tile) return;
+      // The ring tensors' words of this tile.
+      if constexpr (N_RING > 0) {
+        int t = 0;
+        auto ring_read = [&](RabRegs& rg, int tt) {
+          const char* base = smem_sq[tt * RING + cur] + ring_off;
+#pragma unroll
+          for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) rg[jb][a] = *(const u32x2_t*)(base + 16 * ((4 * jb + a) ^ ring_swz));
+        };
+        if constexpr (R_LDS) ring_read(rv, t++);
+        if constexpr (M_LDS) ring_read(mv, t++);
+      }
 
       const char* kbuf = kv_smem(bufc, 0);
       const char* vbuf = kv_smem(bufc, 1);
@@ -954,12 +1058,24 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         }
         return y;
       };
+      // The user mask's value of element r of block jb. On masked tiles the
+      // ring can hold bytes past the sequence (whatever the tensor holds
+      // there): masked keys take 0 there, so P stays 0.
+      auto mval = [&](auto masked, int jb, int r) -> float {
+        float m = sq_val(mv, jb, r);
+        if constexpr (M_LDS && decltype(masked)::value) {
+          const int off = 8 * (r / 4) + (r % 4);
+          const int keep = (int)(vis[jb] << (31 - off)) >> 31;
+          m = __builtin_bit_cast(float, __builtin_bit_cast(int, m) & keep);
+        }
+        return m;
+      };
       // Epilogue of element r of block jb: rab, mask (masked tiles), SiLU, round.
       auto epi = [&](auto masked, int jb, int r) {
         const float y = epi_pre(masked, jb, r);
         const float e = __builtin_amdgcn_exp2f(y);
         float pv = y * __builtin_amdgcn_rcpf(1.f + e);
-        if constexpr (MSK) pv *= sq_val(mv, jb, r);
+        if constexpr (MSK) pv *= mval(masked, jb, r);
         pf[jb][r / 8][r % 8] = (T)pv;
       };
       // The same for the 16 elements of block jb, one operation at a time
@@ -986,7 +1102,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
           for (int r = 0; r < EB; ++r) {
             float pv = y[r] * e[r];
-            if constexpr (MSK) pv *= sq_val(mv, jb, r0 + r);
+            if constexpr (MSK) pv *= mval(masked, jb, r0 + r);
             pf[jb][(r0 + r) / 8][(r0 + r) % 8] = (T)pv;
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1812,8 +1928,25 @@ int num_cus() {
 
 using KernelFn = void (*)(KParams);
 
+// LDS bytes of fwd_kernel's two K/V buffers (the kernel's row padding and
+// 1 KB DMA blocks), and whether n side-tensor rings of three tiles fit
+// beside them at the kernel's occupancy (two workgroups per CU when WPE is
+// 2, one when it is 1; 160 KB of LDS per CU).
+template <int D, int BN>
+constexpr int kv_lds_bytes() {
+  constexpr int ROW_B = D * 2;
+  constexpr int KS_B = ROW_B + 16, VS_B = ROW_B + (ROW_B % 256 == 64 ? 0 : 64);
+  return 2 * ((BN * KS_B + 1023) / 1024 * 1024 + (BN * VS_B + 1023) / 1024 * 1024);
+}
+template <int D, int BN, int WPE>
+constexpr bool ring_fits(int n) {
+  return kv_lds_bytes<D, BN>() + n * 3 * kWaves * kRowsPerWave * BN * 2 + 256 <= (WPE == 2 ? 80 : 160) * 1024;
+}
+
+// sq16: rows of max_seq_len elements are 16-byte multiples, so rab and the
+// user mask can go through the LDS ring (see fwd_kernel's SQL).
 template <typename T, int D, bool PAGED>
-KernelFn pick16(bool causal, bool rab, bool ksplit, bool user_mask, bool delta) {
+KernelFn pick16(bool causal, bool rab, bool ksplit, bool user_mask, bool delta, bool sq16) {
   constexpr int BN = D >= 256 ? 32 : 64;
   constexpr int WPE = D >= 256 ? 1 : 2;
   if (PAGED) return causal ? fwd_kernel<T, D, BN, true, false, true, WPE, 1> : fwd_kernel<T, D, BN, false, false, true, WPE, 1>;
@@ -1823,8 +1956,14 @@ KernelFn pick16(bool causal, bool rab, bool ksplit, bool user_mask, bool delta) 
     // and S^T / P registers: measured 86 -> 67 us on the user-mask workload
     // (64-key tiles spilled at two waves per SIMD and ran best at one).
     constexpr int BNM = D == 128 ? 32 : BN;
-    return rab ? fwd_kernel<T, D, BNM, false, true, false, WPE, 1, true>
-               : fwd_kernel<T, D, BNM, false, false, false, WPE, 1, true>;
+    // The ring takes the mask, and rab too where both fit.
+    constexpr int SQ2 = ring_fits<D, BNM, WPE>(2) ? 3 : ring_fits<D, BNM, WPE>(1) ? 2 : 0;
+    constexpr int SQ1 = ring_fits<D, BNM, WPE>(1) ? 2 : 0;
+    if (rab)
+      return sq16 ? fwd_kernel<T, D, BNM, false, true, false, WPE, 1, true, SQ2>
+                  : fwd_kernel<T, D, BNM, false, true, false, WPE, 1, true>;
+    return sq16 ? fwd_kernel<T, D, BNM, false, false, false, WPE, 1, true, SQ1>
+                : fwd_kernel<T, D, BNM, false, false, false, WPE, 1, true>;
   }
   if constexpr (BN == 64) {
     if (ksplit) {
@@ -1839,12 +1978,17 @@ KernelFn pick16(bool causal, bool rab, bool ksplit, bool user_mask, bool delta) 
   constexpr int BNR = D == 128 ? 32 : BN;
   // Calls with separate key offsets (few queries, long key-split items)
   // measured 6 % faster on 32-key tiles at head_dim 128 as well.
-  if (delta) {
-    if (causal) return rab ? fwd_kernel<T, D, BNR, true, true, false, WPE, 1> : fwd_kernel<T, D, BNR, true, false, false, WPE, 1>;
-    return rab ? fwd_kernel<T, D, BNR, false, true, false, WPE, 1> : fwd_kernel<T, D, BNR, false, false, false, WPE, 1>;
+  // rab through the LDS ring where it fits.
+  constexpr int SQR = ring_fits<D, BNR, WPE>(1) ? 1 : 0;
+  if (rab) {
+    if (causal)
+      return sq16 ? fwd_kernel<T, D, BNR, true, true, false, WPE, 1, false, SQR>
+                  : fwd_kernel<T, D, BNR, true, true, false, WPE, 1>;
+    return sq16 ? fwd_kernel<T, D, BNR, false, true, false, WPE, 1, false, SQR>
+                : fwd_kernel<T, D, BNR, false, true, false, WPE, 1>;
   }
-  if (causal) return rab ? fwd_kernel<T, D, BNR, true, true, false, WPE, 1> : fwd_kernel<T, D, BN, true, false, false, WPE, 1>;
-  return rab ? fwd_kernel<T, D, BNR, false, true, false, WPE, 1> : fwd_kernel<T, D, BN, false, false, false, WPE, 1>;
+  if (delta) return causal ? fwd_kernel<T, D, BNR, true, false, false, WPE, 1> : fwd_kernel<T, D, BNR, false, false, false, WPE, 1>;
+  return causal ? fwd_kernel<T, D, BN, true, false, false, WPE, 1> : fwd_kernel<T, D, BN, false, false, false, WPE, 1>;
 }
 
 template <int D, bool PAGED>
@@ -1860,8 +2004,8 @@ KernelFn pick32(bool causal, bool rab) {
 // jagged with separate key offsets.
 // On return, *wgs_per_cu and *threads give the launch shape.
 template <bool PAGED>
-KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, bool user_mask, bool delta, int* wgs_per_cu,
-              int* threads) {
+KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, bool user_mask, bool delta, bool sq16,
+              int* wgs_per_cu, int* threads) {
   if (dt == DType::FP8) {
     // FP8 cast: head_dim 128 jagged calls without rab, user mask or key offsets.
     if (PAGED || D != 128 || rab || user_mask || delta) return nullptr;
@@ -1876,18 +2020,18 @@ KernelFn pick(DType dt, int D, bool causal, bool rab, bool ksplit, bool user_mas
   switch (dt) {
     case DType::BF16:
       switch (D) {
-        case 32: return pick16<__bf16, 32, PAGED>(causal, rab, ksplit, user_mask, delta);
-        case 64: return pick16<__bf16, 64, PAGED>(causal, rab, ksplit, user_mask, delta);
-        case 128: return pick16<__bf16, 128, PAGED>(causal, rab, ksplit, user_mask, delta);
-        case 256: return pick16<__bf16, 256, PAGED>(causal, rab, ksplit, user_mask, delta);
+        case 32: return pick16<__bf16, 32, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
+        case 64: return pick16<__bf16, 64, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
+        case 128: return pick16<__bf16, 128, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
+        case 256: return pick16<__bf16, 256, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
       }
       break;
     case DType::F16:
       switch (D) {
-        case 32: return pick16<_Float16, 32, PAGED>(causal, rab, ksplit, user_mask, delta);
-        case 64: return pick16<_Float16, 64, PAGED>(causal, rab, ksplit, user_mask, delta);
-        case 128: return pick16<_Float16, 128, PAGED>(causal, rab, ksplit, user_mask, delta);
-        case 256: return pick16<_Float16, 256, PAGED>(causal, rab, ksplit, user_mask, delta);
+        case 32: return pick16<_Float16, 32, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
+        case 64: return pick16<_Float16, 64, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
+        case 128: return pick16<_Float16, 128, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
+        case 256: return pick16<_Float16, 256, PAGED>(causal, rab, ksplit, user_mask, delta, sq16);
       }
       break;
     case DType::F32:
@@ -2105,9 +2249,9 @@ hipError_t launch_run(const FwdArgs& a) {
   // kernel: one 8-wave workgroup per CU, each item twice as fast.
   const bool ksplit = upper <= num_cus();
   int per_cu = 2, threads = kThreads;
-  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, false, false, false, &per_cu, &threads)
+  KernelFn fn = a.paged ? pick<true>(a.dtype, a.head_dim, a.causal, false, false, false, false, false, &per_cu, &threads)
                         : pick<false>(a.dtype, a.head_dim, a.causal, a.rab != nullptr, ksplit, a.user_mask,
-                                      a.seq_offsets_k != nullptr, &per_cu, &threads);
+                                      a.seq_offsets_k != nullptr, a.max_seq_len % 8 == 0, &per_cu, &threads);
   if (!fn) return hipErrorInvalidValue;
   const long long cap = (long long)num_cus() * per_cu;
   const int grid = (int)(upper < cap ? upper : cap);

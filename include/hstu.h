@@ -118,13 +118,16 @@ size_t hstu_fwd_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_h
  *                NULL. rab_num_heads is num_heads_q or 1 (the page's rab
  *                broadcast [b, 1, s, s]: one rab for every head). Indexed by
  *                absolute positions (i, j) within the sequence. Entries the
- *                mask removes may be loaded (whole tile rows inside the
- *                sequence are read) but never affect the output, even when
- *                they hold NaN or inf; entries outside the sequence are
- *                never read.
+ *                mask removes may be loaded (whole tile rows are read) but
+ *                never affect the output, even when they hold NaN or inf.
+ *                Rows past the sequence are never read. When max_seq_len is
+ *                a multiple of 8, columns past the sequence may be read too
+ *                (in 16-byte chunks, never past the row's end), with the
+ *                same guarantee; otherwise they are never read.
  *  mask          [batch, mask_num_heads, max_seq_len, max_seq_len] dtype with
  *                HSTU_MASK_CUSTOM, else NULL. mask_num_heads is num_heads_q or
- *                1; indexed as rab. f16/bf16 only.
+ *                1; indexed and read as rab (masked entries and columns
+ *                past the sequence never affect the output). f16/bf16 only.
  *  out           [Tq, num_heads_q, head_dim]   dtype, bf16 for HSTU_FP8_E4M3
  *                (written for every query)
  *  seq_offsets   [batch + 1] int32, non-decreasing, seq_offsets[0] == 0.

@@ -302,10 +302,14 @@ def test_every_row_is_written(dev):
     assert_parity(got, oracle_jagged(c), "bf16", "nan-prefilled out")
 
 
-def test_masked_rab_nan_is_never_read(dev):
+@pytest.mark.parametrize("S", [140, 144])
+def test_masked_rab_nan_is_never_read(dev, S):
+    """NaN in masked rab entries and in the padding never reaches the output
+    (bit-identical to the run with those entries zero). S = 144 stages rab
+    through the LDS ring, which reads padding columns of the last tiles."""
     c = wl.jagged_case(6, [130, 70], 2, 2, 128, "bf16", num_context=(2, 6), num_targets=(3, 9), target_group_size=1,
-                       rab_std=0.3, max_seq_len=140)
-    say("masked_rab_nan")
+                       rab_std=0.3, max_seq_len=S)
+    say("masked_rab_nan S", S)
     import oracle
     clean = c.rab.clone()
     poisoned = c.rab.clone()
@@ -744,3 +748,38 @@ def test_local_window_workload_reduced_and_sampled(dev):
     ref = oracle_jagged_sampled(c, _picks(c))
     for b, (toks, heads, vals) in ref.items():
         assert_parity(got[torch.as_tensor(toks), torch.as_tensor(heads)], vals, "f16", f"fp16_gqa_local seq {b}")
+
+
+# ------------------------------------------------------------ rab / user mask through the LDS ring
+# max_seq_len a multiple of 8 takes the ring (tiles of rab and the mask staged
+# through LDS by DMA); 304 is not a multiple of the 32- or 64-key tile, so the
+# last tiles reach past the row end (those chunks are clamped and masked).
+RING_MIX = [int(x) for x in np.resize([0, 1, 7, 31, 32, 33, 63, 64, 65, 130, 200, 255, 257, 300, 304], 45)]
+RING = [
+    # (name, lengths, Hq, Hk, D, dtype, mask, nc, nt, g, rab_std, rab_heads, mask_keep, mask_heads, S)
+    ("ring_rab_causal_ctx_targets", RING_MIX, 4, 4, 128, "bf16", CAUSAL, (0, 12), (0, 40), 1, 0.5, None, None, None, 304),
+    ("ring_rab_gqa_f16", RING_MIX, 8, 2, 128, "f16", CAUSAL, None, (1, 30), 3, 0.5, None, None, None, 304),
+    ("ring_rab_bcast_bidirectional", [150, 270, 33, 304], 4, 4, 128, "bf16", NONE, None, None, 0, 0.5, 1, None, None, 304),
+    ("ring_rab_d32", [150, 270, 33, 1], 4, 2, 32, "bf16", CAUSAL, None, (1, 9), 1, 0.5, None, None, None, 272),
+    ("ring_rab_d256", [150, 270, 33, 1], 2, 2, 256, "f16", CAUSAL, None, (1, 9), 1, 0.5, None, None, None, 272),
+    ("ring_mask_only", RING_MIX, 4, 4, 128, "bf16", CUSTOM, None, None, 0, None, None, 0.5, None, 304),
+    ("ring_mask_rab", RING_MIX, 4, 4, 128, "f16", CUSTOM, None, None, 0, 0.3, 1, 0.5, None, 304),
+    ("ring_mask_gqa_d32", [150, 270, 33, 1, 64], 8, 2, 32, "bf16", CUSTOM, None, None, 0, 0.3, None, 0.6, 1, 272),
+    ("ring_mask_d256", [150, 270, 33], 2, 2, 256, "bf16", CUSTOM, None, None, 0, 0.3, 2, 0.5, 2, 272),
+]
+
+
+@pytest.mark.parametrize("case", RING, ids=[e[0] for e in RING])
+def test_ring_rab_and_mask(dev, case):
+    """rab and the user mask staged through the LDS ring (max_seq_len a
+    multiple of 8), element by element against the oracle; NaN fills the
+    rab and mask entries outside each sequence, so any byte of the padding
+    that reached the arithmetic would poison the output."""
+    name, lengths, Hq, Hk, D, dt, mask, nc, nt, g, rab_std, rab_h, keep, mask_h, S = case
+    seed = zlib.crc32(name.encode()) & 0xffff
+    say(name, "seed", seed, "S", S, "batch", len(lengths))
+    c = wl.jagged_case(seed, lengths, Hq, Hk, D, dt, mask_type=mask, num_context=nc, num_targets=nt,
+                       target_group_size=g, rab_std=rab_std, rab_heads=rab_h, mask_keep=keep, mask_heads=mask_h,
+                       max_seq_len=S, name=name)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), dt, name)
