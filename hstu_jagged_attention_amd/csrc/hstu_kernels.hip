@@ -62,6 +62,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kMaxBins = 1024;  // > max key tiles of one row (20480 / 32)
 constexpr int kPlanThreads = 1024;
+static_assert(kMaxBins == kPlanThreads, "the planner keeps one cost bin per thread");
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
@@ -90,7 +91,7 @@ struct KParams {
   int32_t* items;     // work list, two ints per entry (see the planner)
   int32_t* n_items;   // number of valid list entries
   float* partials;    // split items: fp32 partial O, one slot per (chunk, head group)
-  int32_t* split_items;  // split items: two ints each (see the planner)
+  int32_t* split_items;  // split items: four ints each (see the planner)
   int32_t* n_split;      // number of split items
   int32_t split_slots;   // partial-sum slots available (0: never split)
   int32_t target_chunks; // chunks the planner aims for (one per two resident workgroups)
@@ -216,7 +217,9 @@ __device__ inline int nth_tile(const Tiles& t, int n) {
 // (chunk << 24) | (n_chunks << 16) | slot, where `slot` is the first of the
 // n_chunks partial-sum slots of a split item (0xffff when not split).
 // Split items are also listed once each in the reduction list:
-// (b << 16) | q_tile, (n_chunks << 16) | slot.
+// (b << 16) | q_tile, (n_chunks << 16) | slot, the row of the sequence's
+// first query, and its query count (at most half as many entries as slots,
+// so the list fits the two ints per slot the workspace reserves).
 // Chunk size: the total work over target_chunks (one chunk per two resident
 // workgroups; at least kMinChunkTiles), doubled until the split items fit
 // the partial-sum slots.
@@ -275,15 +278,15 @@ constexpr int kCostCache = 4096;  // items whose cost the planner keeps in LDS
 constexpr int kSeqCache = 2048;   // sequences whose lengths the planner keeps in LDS
 
 
-template <bool PAGED>
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, int causal) {
+// BN: the key-tile size costs are counted in (32 or 64).
+template <bool PAGED, int BN>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int causal) {
   __shared__ int hist[kMaxBins];  // items per cost, then chunks per cost
-  __shared__ int scan[2][kMaxBins];
   __shared__ short cost_cache[kCostCache];
   // Per-sequence lengths (Lq, Lh, H, nc), loaded once: the item loops below
   // touch every (sequence, q tile) pair, most of which may lie past the end
   // of their sequence (the q-tile bound comes from max_seq_len).
-  __shared__ int seq_lq[kSeqCache], seq_lh[kSeqCache], seq_h[kSeqCache], seq_nc[kSeqCache];
+  __shared__ int seq_lq[kSeqCache], seq_lh[kSeqCache], seq_h[kSeqCache], seq_nc[kSeqCache], seq_q0[kSeqCache];
   __shared__ int count, total_cost, chunk_tiles, slot_alloc, n_split, qt_bound;
   const int tid = threadIdx.x;
   hist[tid] = 0;
@@ -303,6 +306,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
     if (b < p.batch && b < kSeqCache) {
       const Seq s = load_seq<PAGED>(p, b, causal != 0);
       seq_lq[b] = s.Lq;
+      seq_q0[b] = s.q_tok0;
       seq_lh[b] = s.Lh;
       seq_h[b] = s.H;
       seq_nc[b] = s.nc;
@@ -317,7 +321,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
   auto seq_of = [&](int b) -> Seq {
     if (b >= kSeqCache) return load_seq<PAGED>(p, b, causal != 0);
     Seq s;
-    s.q_tok0 = s.k_tok0 = s.page0 = 0;  // not used for costing
+    s.k_tok0 = s.page0 = 0;  // not used for costing
+    s.q_tok0 = seq_q0[b];
     s.Lq = seq_lq[b];
     s.Lh = seq_lh[b];
     s.L = s.Lh + s.Lq;
@@ -325,76 +330,93 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
     s.nc = seq_nc[b];
     return s;
   };
+  // idx / n_qt through a float reciprocal (idx < 2^24, so the estimate is
+  // off by at most one and one correction step makes it exact).
+  const float inv_nqt = 1.0f / (float)max(n_qt, 1);
+  auto split_idx = [&](int idx, int& b, int& qt) {
+    b = (int)((float)idx * inv_nqt);
+    if (b * n_qt > idx) --b;
+    else if ((b + 1) * n_qt <= idx) ++b;
+    qt = idx - b * n_qt;
+  };
   auto compute_cost = [&](int idx) -> int {  // -1: no such item
-    const int b = idx / n_qt, qt = idx - b * n_qt;
+    int b, qt;
+    split_idx(idx, b, qt);
     const Seq s = seq_of(b);
     const int q_lo = qt * p.bm;
     if (q_lo >= s.Lq) return -1;
     const int i_lo = s.Lh + q_lo, i_hi = s.Lh + min(q_lo + p.bm, s.Lq) - 1;
-    return min(tile_count(tile_range(s, i_lo, i_hi, p.g, p.win, causal != 0, bn)), kMaxBins - 1);
+    return min(tile_count(tile_range(s, i_lo, i_hi, p.g, p.win, causal != 0, BN)), kMaxBins - 1);
   };
   auto cost_of = [&](int idx) -> int { return idx < kCostCache ? (int)cost_cache[idx] : compute_cost(idx); };
   for (int base = 0; base < n_items; base += kPlanThreads) {  // uniform trip count: wave ops below
     const int idx = base + tid;
     const int c = idx < n_items ? compute_cost(idx) : -1;
     if (idx < kCostCache && idx < n_items) cost_cache[idx] = (short)c;
-    if (c > 0) atomicAdd(&hist[c], 1);
+    if (c >= 0) atomicAdd(&hist[c], 1);
     wave_fetch_add(&total_cost, max(c, 0));
+    wave_fetch_add(&count, c >= 0 ? 1 : 0);
   }
   __syncthreads();
   // Chunk size from the cost histogram (no further pass over the items):
-  // candidates t0, 2 t0, 4 t0, ... are evaluated together, one histogram
-  // bin per thread; the first whose split items fit the slots wins.
+  // candidates t0, 2 t0, 4 t0, ... in turn, one histogram bin per thread;
+  // the first whose split items fit the slots wins (usually the first).
   constexpr int kCand = 10;  // t0 << 9 >= kMaxBins: the last candidate never splits
   __shared__ int need[kCand];
   if (tid < kCand) need[tid] = 0;
+  if (tid == 0) chunk_tiles = INT_MAX;
   __syncthreads();
   const long long units = (long long)total_cost * p.n_hg;
   const int t0 = (int)min((long long)kMaxBins,
                           max((long long)kMinChunkTiles, (units + p.target_chunks - 1) / p.target_chunks));
-  if (p.split_slots > 0) {  // uniform: every thread takes part in the wave sums
+  if (p.split_slots > 0) {  // uniform: every thread takes part in the wave sums and barriers
     const int h = hist[tid];
-#pragma unroll
+    // Chunks of a cost-tid item at chunk size t0 << ci: ceil(tid / t0)
+    // halved ci times (rounding up), which is ceil(tid / (t0 << ci)).
+    const int q0 = (tid + t0 - 1) / t0;
     for (int ci = 0; ci < kCand; ++ci) {
       const int t = t0 << ci;
-      wave_fetch_add(&need[ci], (h > 0 && tid > t) ? min(h * min((tid + t - 1) / t, 255), 1 << 24) : 0);
+      const int nk = (q0 + (1 << ci) - 1) >> ci;
+      wave_fetch_add(&need[ci], (h > 0 && tid > t) ? min(h * min(nk, 255), 1 << 24) : 0);
+      __syncthreads();
+      if (need[ci] <= p.split_slots) {  // the same value in every thread
+        if (tid == 0) chunk_tiles = t;
+        break;
+      }
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int t = INT_MAX;
-    if (p.split_slots > 0) {
-      for (int ci = kCand - 1; ci >= 0; --ci)
-        if (need[ci] <= p.split_slots) t = t0 << ci;
-    }
-    chunk_tiles = t;
   }
   __syncthreads();
   const int T = chunk_tiles;
   auto n_chunks = [&](int c) { return c > T ? min((c + T - 1) / T, 255) : 1; };
-  hist[tid] = 0;
-  __syncthreads();
-  for (int base = 0; base < n_items; base += kPlanThreads) {
-    const int idx = base + tid;
-    const int c = idx < n_items ? cost_of(idx) : -1;
-    const int nk = c < 0 ? 0 : n_chunks(c);
-    for (int k = 0; k < nk; ++k) atomicAdd(&hist[(k + 1) * c / nk - k * c / nk], 1);
-    wave_fetch_add(&count, nk);
-  }
-  __syncthreads();
-  // Exclusive scan over bins in descending cost: start[c] = sum of hist[c'] for c' > c.
-  int buf = 0;
-  scan[0][tid] = tid == 0 ? 0 : hist[kMaxBins - tid];
-  __syncthreads();
-  for (int off = 1; off < kMaxBins; off <<= 1) {
-    int x = scan[buf][tid];
-    if (tid >= off) x += scan[buf][tid - off];
-    scan[buf ^ 1][tid] = x;
-    buf ^= 1;
+  // Cost of chunk k of nk of an item of cost c.
+  auto chunk_cost = [&](int c, int k, int nk) { return nk == 1 ? c : (k + 1) * c / nk - k * c / nk; };
+  if (T != INT_MAX) {  // uniform; without splits the histogram and count above already hold
+    if (tid == 0) count = 0;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int base = 0; base < n_items; base += kPlanThreads) {
+      const int idx = base + tid;
+      const int c = idx < n_items ? cost_of(idx) : -1;
+      const int nk = c < 0 ? 0 : n_chunks(c);
+      for (int k = 0; k < nk; ++k) atomicAdd(&hist[chunk_cost(c, k, nk)], 1);
+      wave_fetch_add(&count, nk);
+    }
     __syncthreads();
   }
-  hist[tid] = scan[buf][kMaxBins - 1 - tid];
-  __syncthreads();
+  // Exclusive scan over bins in descending cost: start[c] = sum of hist[c']
+  // for c' > c. Thread tid holds bin kMaxBins - 1 - tid: a wave-wide scan of
+  // 64 bins, then the sums of the waves before.
+  __shared__ int wave_tot[kPlanThreads / 64];
+  {
+    const int own = hist[kMaxBins - 1 - tid];
+    const int inc = wave_inclusive_sum(own);
+    if ((tid & 63) == 63) wave_tot[tid >> 6] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
+    hist[kMaxBins - 1 - tid] = before + inc - own;
+    __syncthreads();
+  }
   for (int base = 0; base < n_items; base += kPlanThreads) {
     const int idx = base + tid;
     const int c = idx < n_items ? cost_of(idx) : -1;
@@ -403,15 +425,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int bn, i
     const int slot_at = wave_fetch_add(&slot_alloc, split_nk);
     const int split_at = wave_fetch_add(&n_split, split_nk ? 1 : 0);
     if (c < 0) continue;
-    const int b = idx / n_qt, qt = idx - b * n_qt;
+    int b, qt;
+    split_idx(idx, b, qt);
     int slot = 0xffff;
     if (nk > 1) {
       slot = slot_at;
-      p.split_items[2 * split_at] = (b << 16) | qt;
-      p.split_items[2 * split_at + 1] = (nk << 16) | slot;
+      // The reduction reads the entry whole: no sequence loads there.
+      const Seq s = seq_of(b);
+      p.split_items[4 * split_at] = (b << 16) | qt;
+      p.split_items[4 * split_at + 1] = (nk << 16) | slot;
+      p.split_items[4 * split_at + 2] = s.q_tok0;
+      p.split_items[4 * split_at + 3] = s.Lq;
     }
     for (int k = 0; k < nk; ++k) {
-      const int pos = atomicAdd(&hist[(k + 1) * c / nk - k * c / nk], 1);
+      const int pos = atomicAdd(&hist[chunk_cost(c, k, nk)], 1);
       p.items[2 * pos] = (b << 16) | qt;
       p.items[2 * pos + 1] = (k << 24) | (nk << 16) | slot;
     }
@@ -1653,14 +1680,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p) {
   constexpr int SLOT_FLOATS = kWaves * kRowsPerWave * D;
-  const int n_work = *p.n_split * p.n_hg;
   const int hpw = 1 << p.hpw_log2;
+  // The first entry is read together with the count (every workgroup's
+  // first entry lies inside the split list: the grid is at most half the
+  // slots times the head groups), so the two loads overlap.
+  auto entry = [&](int it) { return *(const u32x4_t*)(p.split_items + 4 * it); };
+  u32x4_t e = entry(blockIdx.x / p.n_hg);
+  const int n_work = *p.n_split * p.n_hg;
   for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
     const int it = w / p.n_hg, hg = w - it * p.n_hg;
-    const int packed = p.split_items[2 * it], meta = p.split_items[2 * it + 1];
-    const int b = packed >> 16, qt = packed & 0xffff;
+    if (w != (int)blockIdx.x) e = entry(it);
+    const int packed = (int)e[0], meta = (int)e[1];
+    const int qt = packed & 0xffff;
     const int nk = (meta >> 16) & 0xff, slot0 = meta & 0xffff;
-    const Seq s = load_seq<PAGED>(p, b, false);
+    const int q_tok0 = (int)e[2], Lq = (int)e[3];
     const int q_lo = qt * p.bm;
     const float* base = p.partials + ((size_t)slot0 * p.n_hg + hg) * SLOT_FLOATS;
     const size_t chunk_stride = (size_t)p.n_hg * SLOT_FLOATS;
@@ -1669,7 +1702,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p) {
       const int row = (f / D) % kRowsPerWave;
       const int d = f % D;
       const int q_loc = q_lo + (wv >> p.hpw_log2) * kRowsPerWave + row;
-      if (q_loc >= s.Lq) continue;
+      if (q_loc >= Lq) continue;
       const int h = hg * hpw + (wv & (hpw - 1));
       f32x4_t acc = *(const f32x4_t*)(base + f);
       for (int k = 1; k < nk; ++k) {
@@ -1680,7 +1713,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p) {
       T y[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = (T)(acc[e] * p.out_mul);
-      *(u32x2_t*)((T*)p.out + ((size_t)(s.q_tok0 + q_loc) * p.Hq + h) * D + d) = *(const u32x2_t*)y;
+      *(u32x2_t*)((T*)p.out + ((size_t)(q_tok0 + q_loc) * p.Hq + h) * D + d) = *(const u32x2_t*)y;
     }
   }
 }
@@ -2233,11 +2266,18 @@ hipError_t launch_validate(const FwdArgs& a, int32_t* flag) {
 hipError_t launch_plan(const FwdArgs& a) {
   const KParams p = make_params(a);
   if (use_direct(a, p)) return hipSuccess;
-  const int bn = tile_n(a);
-  if (a.paged)
-    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, a.stream, p, bn, a.causal ? 1 : 0);
-  else
-    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, a.stream, p, bn, a.causal ? 1 : 0);
+  const int causal = a.causal ? 1 : 0;
+  if (tile_n(a) == 32) {
+    if (a.paged)
+      hipLaunchKernelGGL((plan_kernel<true, 32>), dim3(1), dim3(kPlanThreads), 0, a.stream, p, causal);
+    else
+      hipLaunchKernelGGL((plan_kernel<false, 32>), dim3(1), dim3(kPlanThreads), 0, a.stream, p, causal);
+  } else {
+    if (a.paged)
+      hipLaunchKernelGGL((plan_kernel<true, 64>), dim3(1), dim3(kPlanThreads), 0, a.stream, p, causal);
+    else
+      hipLaunchKernelGGL((plan_kernel<false, 64>), dim3(1), dim3(kPlanThreads), 0, a.stream, p, causal);
+  }
   return hipGetLastError();
 }
 
