@@ -61,6 +61,13 @@ def parse():
     ap.add_argument("--counter-summary", nargs="+", metavar=("WORKLOAD", "DIR"),
                     help="CPU only: turn rocprofv3 --pmc output folders (the passes of COUNTER_PASSES) into "
                          "profiles/counters_<WORKLOAD>.txt")
+    ap.add_argument("--stats-summary", nargs=3, metavar=("WORKLOAD", "TRACE_DIR", "BENCH_OUT"),
+                    help="CPU only: turn a rocprofv3 --kernel-trace --stats output folder of this script on "
+                         "WORKLOAD (and the JSON line that run printed, saved in BENCH_OUT) into "
+                         "profiles/kernels_<WORKLOAD>_stats.txt")
+    ap.add_argument("--default-command", action="store_true",
+                    help="with --stats-summary: the traced run was the default command (no flags); the summary "
+                         "goes to profiles/fwd_kernel_<WORKLOAD>_stats.txt")
     ap.add_argument("--traffic-record", nargs=5, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                           "COPY_WRITE_DIR"),
                     help="CPU only: turn the four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of this "
@@ -98,6 +105,11 @@ def measured_traffic(name):
     return rec.get("traffic_bytes_per_launch")
 
 
+def is_fwd(kernel_name):
+    """The forward kernel's dispatches (16-bit / fp32 fwd_kernel or the FP8 fwd_fp8_kernel)."""
+    return "fwd_kernel" in kernel_name or "fwd_fp8_kernel" in kernel_name
+
+
 def _counter_rows(folder, counter):
     """(kernel name, value) of every dispatch in the rocprofv3 counter CSVs under folder."""
     import csv
@@ -125,13 +137,14 @@ def traffic_record(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     cw = [v for k, v in _counter_rows(copy_write_dir, "WRITE_SIZE") if "copyBuffer" in k]
     fetch_factor = copy_kib / statistics.mean(cf)
     write_factor = copy_kib / statistics.mean(cw)
-    fk = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if "fwd_kernel" in k]
-    wk = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if "fwd_kernel" in k]
+    fk = [v for k, v in _counter_rows(fetch_dir, "FETCH_SIZE") if is_fwd(k)]
+    wk = [v for k, v in _counter_rows(write_dir, "WRITE_SIZE") if is_fwd(k)]
     fetch, write = statistics.mean(fk), statistics.mean(wk)
     traffic = (fetch * fetch_factor + write * write_factor) * 1024.0
     from hstu_jagged_attention_amd import workloads as wl
     _, alg_bytes, _ = workload_work(name, wl.WORKLOADS[name]())
-    rec = {"workload": name, "kernel": "fwd_kernel", "kernel_source_sha256": kernel_source_sha256(),
+    fwd_name = "fwd_fp8_kernel" if name.startswith("fp8") else "fwd_kernel"
+    rec = {"workload": name, "kernel": fwd_name, "kernel_source_sha256": kernel_source_sha256(),
            "fetch_kib_per_dispatch": round(fetch, 3), "write_kib_per_dispatch": round(write, 3),
            "fetch_factor": round(fetch_factor, 5), "write_factor": round(write_factor, 5),
            "traffic_bytes_per_launch": int(round(traffic)), "algorithmic_bytes_per_launch": int(round(alg_bytes)),
@@ -191,7 +204,7 @@ def counter_summary(name, folders):
         for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
-                    if "fwd_kernel" not in r["Kernel_Name"]:
+                    if not is_fwd(r["Kernel_Name"]):
                         continue
                     kernels.add(r["Kernel_Name"].split("(")[0][:120])
                     vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -235,6 +248,80 @@ def counter_summary(name, folders):
     lines.append("")
     out = os.path.join(ROOT, "profiles", f"counters_{name}.txt")
     with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def stats_summary(name, trace_dir, bench_out, default_command=False):
+    """Writes the kernel-trace summary of one bench run: rocprofv3's
+    per-kernel statistics, and the forward kernel's mean duration over its
+    cold dispatches (those that follow the cache flush, directly or after
+    the plan kernel, as in the timed steps and the run-phase timing) and over
+    the others (warm), to set beside the bench line's launch_ms_mean and
+    launch_ms_mean_warm."""
+    import csv
+    import glob
+    import statistics
+
+    def one(pattern):
+        files = sorted(glob.glob(os.path.join(trace_dir, "**", pattern), recursive=True))
+        if not files:
+            raise SystemExit(f"no {pattern} under {trace_dir}")
+        return files[0]
+    with open(one("*kernel_stats.csv")) as f:
+        stats = list(csv.DictReader(f))
+    with open(one("*kernel_trace.csv")) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    with open(bench_out) as f:
+        line = next(json.loads(x) for x in f if x.startswith("{") and '"metric"' in x)
+    cold, warm, prev = [], [], []
+    for r in trace:
+        kn = r["Kernel_Name"]
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if is_fwd(kn):
+            after_flush = prev and ("FillFunctor" in prev[-1] or ("plan_kernel" in prev[-1] and len(prev) > 1
+                                                                  and "FillFunctor" in prev[-2]))
+            (cold if after_flush else warm).append(dur)
+        prev.append(kn)
+    total = sum(float(r["TotalDurationNs"]) for r in stats)
+
+    def short(kn):
+        kn = kn.replace("(anonymous namespace)::", "")
+        return (kn[:84] + "...") if len(kn) > 87 else kn
+    cmd = "python3 REPO/bench.py" + ("" if default_command else f" --workload {name} --steps 30 --warmup 5 "
+                                                                "--no-cpu-baseline")
+    r = line["roofline"]
+    lines = [f"Kernels of workload {name}: rocprofv3 kernel-trace statistics of "
+             + ("the default bench command" if default_command else "one bench run"), "",
+             "Command (run from /tmp with TMPDIR=/tmp; REPO = repository root, OUT = any output folder):",
+             f"  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats_{name} -o run -- {cmd} "
+             "> OUT/bench_{name}.out".replace("{name}", name),
+             f"  python3 REPO/bench.py --stats-summary {name} OUT/stats_{name} OUT/bench_{name}.out"
+             + (" --default-command" if default_command else "") + "   (this summary)",
+             "(the run does warmup + steps cold plan/run pairs, each after a 1 GiB cache flush, then cold run-only "
+             "launches, then warm back-to-back steps, runs and plans; durations in microseconds)", "",
+             f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for row in sorted(stats, key=lambda x: -float(x["TotalDurationNs"])):
+        lines.append(f"{short(row['Name']):90s} {int(row['Calls']):6d} {float(row['AverageNs']) / 1e3:9.3f} "
+                     f"{float(row['MinNs']) / 1e3:9.3f} {float(row['MaxNs']) / 1e3:9.3f} "
+                     f"{100 * float(row['TotalDurationNs']) / total:6.2f}")
+    lines += ["", "fwd_kernel dispatches by cache state (from the per-dispatch trace):",
+              f"  cold (after the flush): {len(cold):4d} dispatches, mean {statistics.mean(cold):9.3f} us"
+              if cold else "  cold: none",
+              f"  warm:                   {len(warm):4d} dispatches, mean {statistics.mean(warm):9.3f} us"
+              if warm else "  warm: none", "",
+              "bench.py line printed by the same run:",
+              f"  value {line['value']} {line['unit']}, ms_per_step {line['ms_per_step']} (cold), "
+              f"warm_ms_per_step {line.get('warm_ms_per_step')}",
+              f"  roofline: bound {r['bound']}, achieved {r['achieved']} {r['unit']}, frac {r['frac']}, "
+              f"launch_ms_mean {r['launch_ms_mean']} (cold run phase: {r['kernel']}), "
+              f"launch_ms_mean_warm {r.get('launch_ms_mean_warm')}, plan {r.get('plan_kernel_ms_mean_warm')} ms"]
+    if "cpu_baseline" in line:
+        cb = line["cpu_baseline"]
+        lines.append(f"  cpu_baseline {cb['value']} {cb['unit']} ({cb['kind']}, {cb['cores']} threads; {cb['sample']})")
+    lines.append("")
+    fname = f"fwd_kernel_{name}_stats.txt" if default_command else f"kernels_{name}_stats.txt"
+    with open(os.path.join(ROOT, "profiles", fname), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -531,7 +618,8 @@ def measure(name, args, dev):
         achieved, peak, unit = hbm_gbs, PEAK_HBM_GBS, "GB/s"
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
-                "kernel": "fwd_kernel" + ("+reduce_kernel" if split_keys(c) else ""),
+                "kernel": ("fwd_fp8_kernel" if c.dtype == "fp8" else "fwd_kernel") +
+                          ("+reduce_kernel" if split_keys(c) else ""),
                 "launch_ms_mean": round(run_ms, 5), "launch_ms_mean_warm": round(warm_run_ms, 5),
                 "plan_kernel_ms_mean_warm": round(plan_ms, 5), "algorithmic_flops": flops,
                 "algorithmic_bytes": alg_bytes, "mfma_tflops": round(mfma_tflops, 3),
@@ -564,6 +652,9 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary[0], args.counter_summary[1:])
+        return
+    if args.stats_summary:
+        stats_summary(*args.stats_summary, default_command=args.default_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the library has no multi-GPU "
