@@ -736,10 +736,15 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     const bool wave_active = q_lo + rb * kRowsPerWave < s.Lq;
     const int i = s.Lh + q_loc;
 
+    // Paged calls: a key tile lies in one cache page when it ends inside the
+    // history and pages hold at least BN rows; its page id is then
+    // page_ids[page0 + j0 / page_size].
+    auto in_page = [&](int j0) { return PAGED && j0 + BN <= s.Lh && (1 << p.ps_log2) >= BN; };
     // Uniform base addresses of a whole tile whose BN rows are consecutive
     // rows of one tensor (stride row_stride_b); false for tiles that end past
     // the sequence, straddle the history / new-token boundary, or span pages.
-    auto tile_bases = [&](int j0, const char*& kb, const char*& vb) -> bool {
+    // page: the tile's page id when in_page(j0).
+    auto tile_bases = [&](int j0, int page, const char*& kb, const char*& vb) -> bool {
       if (!PAGED) {
         if (j0 + BN > s.L) return false;
         const size_t e = ((size_t)(s.k_tok0 + j0) * p.Hk + hk) * D;
@@ -749,7 +754,6 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       } else {
         if (j0 + BN <= s.Lh) {
           if ((1 << p.ps_log2) < BN) return false;
-          const int page = p.page_ids[s.page0 + (j0 >> p.ps_log2)];
           const size_t slot0 = (size_t)(j0 & ((1 << p.ps_log2) - 1));
           const size_t ek = (((((size_t)page * 2) << p.ps_log2) + slot0) * p.Hk + hk) * D;
           const size_t ev = (((((size_t)page * 2 + 1) << p.ps_log2) + slot0) * p.Hk + hk) * D;
@@ -766,13 +770,14 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         return false;
       }
     };
-    // DMA of key tile kt into buffer BUF. Rows past the sequence repeat its
-    // last row (finite values, masked to zero by the epilogue).
-    auto dma_tile = [&](int kt, auto bufc) {
+    // DMA of key tile kt into buffer BUF (page: its page id when in a page).
+    // Rows past the sequence repeat its last row (finite values, masked to
+    // zero by the epilogue).
+    auto dma_tile = [&](int kt, auto bufc, int page) {
       constexpr int BUF = decltype(bufc)::value;
       const int j0 = kt * BN;
       const char *kb, *vb;
-      if (tile_bases(j0, kb, vb)) {
+      if (tile_bases(j0, page, kb, vb)) {
 #pragma unroll
         for (int u = 0; u < K_BLK_W; ++u) {
           const int blk = wave + kWaves * u;
@@ -810,7 +815,26 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     const int n_begin = chunk * n_tiles / n_chunks, n_end = (chunk + 1) * n_tiles / n_chunks;
     const int n_steps = (n_end - n_begin + KSP - 1) / KSP;
     // The first tile's DMA goes out before the Q load, to overlap their latencies.
-    if (n_begin + GRP < n_end) dma_tile(tile_at(n_begin + GRP), Buf0{});
+    if (n_begin + GRP < n_end) {
+      const int j0 = tile_at(n_begin + GRP) * BN;
+      dma_tile(tile_at(n_begin + GRP), Buf0{}, in_page(j0) ? p.page_ids[s.page0 + (j0 >> p.ps_log2)] : 0);
+    }
+    // Paged calls: the page id of the tile a step's DMA fetches is read one
+    // step earlier, by a vector load issued after that step's DMA (so the
+    // next step's wait for its tile covers it); the DMA then needs no
+    // dependent load of its own.
+    int page_v = 0;
+    auto load_page = [&](int n) {
+      if constexpr (PAGED) {
+        const int j0 = tile_at(n) * BN;
+        if (in_page(j0)) {
+          int idx = s.page0 + (j0 >> p.ps_log2);
+          asm volatile("" : "+v"(idx));  // a vector load, counted by vmcnt behind the DMA
+          page_v = p.page_ids[idx];
+        }
+      }
+    };
+    if (n_begin + GRP + KSP < n_end) load_page(n_begin + GRP + KSP);
 
     // Q fragments (B operand of S^T = K Q^T), pre-scaled by c.
     V8 qf[KS];
@@ -963,7 +987,8 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // The next tile's DMA goes out first: it has a whole step to land;
       // then the next tile's rab (this tile's arrived last step), then the
       // ring tile two ahead, into the slot the last step read.
-      if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{});
+      if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{}, __builtin_amdgcn_readfirstlane(page_v));
+      if (n + 2 * KSP < n_end) load_page(n + 2 * KSP);
       RabRegs rv, mv;
       if constexpr (RAB && !R_LDS) {
 #pragma unroll
