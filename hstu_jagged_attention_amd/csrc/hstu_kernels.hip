@@ -594,6 +594,9 @@ __device__ inline v4i16_t lds_read_tr16(const void* addr) {
 }
 
 __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_getreg operand for the whole HW_ID register (id 4, bits 0..31): bits
+// 3:0 are the wave's slot on its SIMD, bits 5:4 the SIMD.
+constexpr int kHwRegHwId = (31 << 11) | 4;
 
 // KSP = 1: a workgroup of 4 waves walks all key tiles of its item.
 // KSP = 2: 8 waves in two groups of 4; group g takes key tiles g, g+2, ...
@@ -660,6 +663,31 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
   const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave = wave_id & (kWaves - 1);  // role inside the key group
   const int l32 = lane & 31, half = lane >> 5;
+  // Logical wave lw (query row block and head of this wave): the rank of
+  // the key (SIMD + 2 x wave-slot parity) mod 4 of this wave among the four
+  // of its key group (ties by wave index), from the hardware id register.
+  // Two workgroups share a CU, in wave slots 0 and 1, one wave per SIMD
+  // each: their logical waves 0 and 1 then sit on different SIMD pairs, so
+  // items with fewer rows than a workgroup holds (few-token paged and
+  // delta-QK calls) do not stack both workgroups' active waves on the same
+  // SIMDs. The ranks form a permutation whatever the placement, and results
+  // do not depend on it.
+  __shared__ int sh_key[kWaves];
+  if (lane == 0 && wave_id < kWaves) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg(kHwRegHwId);
+    sh_key[wave_id] = (int)((((hw >> 4) & 3u) + 2u * (hw & 1u)) & 3u);
+  }
+  __syncthreads();
+  int lw = 0;
+  {
+    const int mine = sh_key[wave];
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) {
+      const int k = sh_key[j];
+      lw += (k < mine || (k == mine && j < wave)) ? 1 : 0;
+    }
+  }
+  lw = __builtin_amdgcn_readfirstlane(lw);
   const bool direct = p.direct_items > 0;
   const int n_work = direct ? p.direct_items : *p.n_items * p.n_hg;
   const int hpw = 1 << p.hpw_log2;
@@ -725,8 +753,8 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     // A direct item past the end of its sequence has no rows; in direct mode
     // every workgroup has exactly one item, so it simply has no work.
     if (direct && qt * p.bm >= s.Lq) break;
-    const int h = hg * hpw + (wave & (hpw - 1));
-    const int rb = wave >> p.hpw_log2;
+    const int h = hg * hpw + (lw & (hpw - 1));
+    const int rb = lw >> p.hpw_log2;
     const int hk = (hg * hpw) / p.group;
     const int q_lo = qt * p.bm;
     const int q_hi = min(q_lo + p.bm, s.Lq);
@@ -916,7 +944,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
     };
     // This lane's rab / mask words of ring slot rs, in the register layout
     // of the prefetch below.
-    const int ring_pair = wave * kRowsPerWave + l32;
+    const int ring_pair = lw * kRowsPerWave + l32;
     const int ring_off = ring_pair * SQ_ROW_B + 8 * half;
     const int ring_swz = (ring_pair / SQ_G) % SQ_CH;
     // rab (or mask) of the tile at key j0: lane holds row q_loc, keys
@@ -1339,7 +1367,7 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // sums the chunks in order (deterministic) and writes O.
       if (row_ok) {
         float* mine = p.partials + ((size_t)(slot0 + chunk) * p.n_hg + hg) * (kWaves * kRowsPerWave * D) +
-                      (size_t)(wave * kRowsPerWave + l32) * D;
+                      (size_t)(lw * kRowsPerWave + l32) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -2255,10 +2283,14 @@ KParams make_params(const FwdArgs& a) {
   p.out_mul = a.dtype == DType::F32 ? a.out_scale * a.alpha : a.dtype == DType::FP8 ? a.out_scale
                                                                                      : -a.out_scale / kLog2e;
   const bool one_wave = a.dtype == DType::F32 || a.head_dim >= 256;
-  // One chunk per two resident workgroups: measured against 4x, 2x, 1/2x and
-  // 1/4x that on the paged and delta-QK workloads (fewer chunks lengthen the
-  // critical path; more of them cost partial-sum traffic and reduction time).
-  p.target_chunks = num_cus() * (one_wave ? 1 : 2) / 2;
+  // Paged calls: one chunk per two resident workgroups; jagged calls with
+  // their own key offsets: one per resident workgroup. Measured on the paged
+  // and delta-QK workloads against 1/4x to 8x that (cold, caches flushed by
+  // a read): fewer chunks lengthen the critical path; more of them cost
+  // chunk set-ups, partial-sum traffic and reduction time, and on the paged
+  // workload slow every step (paged 92.8 us at 1x, 101.6 at 2x, 98.4 at 4x;
+  // delta-QK 39.6 us at 1x, 38.1 at 2x, 51.7 at 4x).
+  p.target_chunks = num_cus() * (one_wave ? 1 : 2) / 2 * (a.paged ? 1 : 2);
   return p;
 }
 
