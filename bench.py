@@ -11,8 +11,9 @@ stream rab, a user mask or a KV cache) and the float64 CPU oracle timed on
 the host as a baseline.
 
 Timing is cold by default: before every timed step a 1 GiB device buffer is
-written (outside the timed events), which evicts the inputs from the L2
-caches and the 256 MB Infinity Cache, so every step reads them from HBM.
+read (outside the timed events), which evicts the inputs from the L2 caches
+and the 256 MB Infinity Cache, so every step reads them from HBM, and leaves
+no dirty lines whose write-back would compete with the step.
 Steps are timed with HIP events on the launch stream. Back-to-back (warm)
 steps are reported as secondary keys.
 
@@ -641,7 +642,7 @@ def measure(name, args, dev):
            "config": dict(workload=name, **desc),
            # the metric's percentage: of the dense bf16 peak (of the fp32 peak for the fp32 workload)
            "pct_of_mfma_peak": round(100 * value / (peak_f if dtype == "f32" else PEAK_TFLOPS["bf16"]), 2),
-           "timing": "cold: a 1 GiB device write before each step (outside the events) evicts L2 and Infinity "
+           "timing": "cold: a 1 GiB device read before each step (outside the events) evicts L2 and Infinity "
                      "Cache; per-step HIP events on the launch stream",
            "ms_per_step_median": round(statistics.median(step_ms), 5),
            "timed_region_wall_ms": round(region_wall_ms, 3),
