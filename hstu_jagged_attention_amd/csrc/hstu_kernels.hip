@@ -1015,7 +1015,35 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
       // The next tile's DMA goes out first: it has a whole step to land;
       // then the next tile's rab (this tile's arrived last step), then the
       // ring tile two ahead, into the slot the last step read.
-      if (n + KSP < n_end) dma_tile(tile_at(n + KSP), std::integral_constant<int, BUF ^ 1>{}, __builtin_amdgcn_readfirstlane(page_v));
+      // Jagged 64-key kernels at two waves per SIMD, no side-tensor ring: a
+      // whole next tile's DMA instructions (K_BLK_W + V_BLK_W per wave) are
+      // spread over the S^T MFMA groups below instead of going out back to
+      // back, where the CU's 80 or so 1 KB LDS DMAs queue behind each other
+      // and each wave stalls until its last one is accepted (GQA workload
+      // about 2 % faster; the shorter steps of 32-key and paged kernels left
+      // too little time after the spread DMAs, so they issue at once).
+      constexpr bool SPREAD = WPE == 2 && N_RING == 0 && BN == 64 && !PAGED;
+      constexpr int NQ = K_BLK_W + V_BLK_W;
+      using NextBuf = std::integral_constant<int, BUF ^ 1>;
+      const char *kb_n = nullptr, *vb_n = nullptr;
+      bool spread = false;
+      if (n + KSP < n_end) {
+        const int kt_n = tile_at(n + KSP), pg = __builtin_amdgcn_readfirstlane(page_v);
+        if (SPREAD && tile_bases(kt_n * BN, pg, kb_n, vb_n))
+          spread = true;
+        else
+          dma_tile(kt_n, NextBuf{}, pg);
+      }
+      // DMA instruction q of this wave for the next tile (whole tiles only).
+      auto dma_part = [&](int q) {
+        if (q < K_BLK_W) {
+          const int blk = wave + kWaves * q;
+          if (K_BLK % kWaves == 0 || blk < K_BLK) dma16(kb_n + dma_k_off[q], kv_smem(NextBuf{}, 0) + blk * 1024);
+        } else {
+          const int u = q - K_BLK_W, blk = wave + kWaves * u;
+          if (V_BLK % kWaves == 0 || blk < V_BLK) dma16(vb_n + dma_v_off[u], kv_smem(NextBuf{}, 1) + blk * 1024);
+        }
+      };
       if (n + 2 * KSP < n_end) load_page(n + 2 * KSP);
       RabRegs rv, mv;
       if constexpr (RAB && !R_LDS) {
@@ -1036,7 +1064,15 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
         asm volatile("" ::: "memory");
         if (n + 2 < n_end) ring_dma(n + 2, cur == 0 ? RING - 1 : cur - 1);
       }
-      if (!wave_active || !has_tile) return;
+      if (!wave_active || !has_tile) {
+        if constexpr (SPREAD) {
+          if (spread) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) dma_part(q);
+          }
+        }
+        return;
+      }
       // The ring tensors' words of this tile.
       if constexpr (N_RING > 0) {
         int t = 0;
@@ -1281,6 +1317,12 @@ __global__ __launch_bounds__(kThreads * KSP) __attribute__((amdgpu_waves_per_eu(
           for (int e = 0; e < GS; ++e) {
             const int q = g * GS + e;
             sacc[q % NJB] = F::mfma(kf[g & 1][e], qf[q / NJB], sacc[q % NJB]);
+          }
+          if constexpr (SPREAD) {
+            if (spread) {
+#pragma unroll
+              for (int q = g * NQ / NGS; q < (g + 1) * NQ / NGS; ++q) dma_part(q);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
