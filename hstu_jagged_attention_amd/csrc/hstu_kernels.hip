@@ -1776,39 +1776,54 @@ template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(KParams p) {
   constexpr int SLOT_FLOATS = kWaves * kRowsPerWave * D;
   const int hpw = 1 << p.hpw_log2;
-  // The first entry is read together with the count (every workgroup's
-  // first entry lies inside the split list: the grid is at most half the
-  // slots times the head groups), so the two loads overlap.
+  // Work unit: (split item, head group, 32-row block of the partial tile);
+  // blocks without rows of the sequence are skipped whole. Each thread sums
+  // its float4s over the chunks in chunk order (deterministic), with the
+  // loads of four chunks in flight at a time. The first entry is read
+  // together with the count (every workgroup's first entry lies inside the
+  // split list's allocation: the grid is at most half the slots times the
+  // head groups and row blocks), so the two loads overlap.
   auto entry = [&](int it) { return *(const u32x4_t*)(p.split_items + 4 * it); };
-  u32x4_t e = entry(blockIdx.x / p.n_hg);
-  const int n_work = *p.n_split * p.n_hg;
+  u32x4_t e = entry(blockIdx.x / (p.n_hg * kWaves));
+  const int n_work = *p.n_split * p.n_hg * kWaves;
   for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int it = w / p.n_hg, hg = w - it * p.n_hg;
+    const int it = w / (p.n_hg * kWaves), rest = w - it * (p.n_hg * kWaves);
+    const int hg = rest / kWaves, wv = rest - hg * kWaves;
     if (w != (int)blockIdx.x) e = entry(it);
     const int packed = (int)e[0], meta = (int)e[1];
     const int qt = packed & 0xffff;
     const int nk = (meta >> 16) & 0xff, slot0 = meta & 0xffff;
     const int q_tok0 = (int)e[2], Lq = (int)e[3];
-    const int q_lo = qt * p.bm;
-    const float* base = p.partials + ((size_t)slot0 * p.n_hg + hg) * SLOT_FLOATS;
+    const int rblk = wv >> p.hpw_log2;
+    const int row0 = qt * p.bm + rblk * kRowsPerWave;
+    const int rows = min(Lq - row0, kRowsPerWave);
+    if (rows <= 0) continue;  // uniform: no rows of the sequence in this block
+    const int h = hg * hpw + (wv & (hpw - 1));
+    const float* base = p.partials + ((size_t)slot0 * p.n_hg + hg) * SLOT_FLOATS + (size_t)wv * kRowsPerWave * D;
     const size_t chunk_stride = (size_t)p.n_hg * SLOT_FLOATS;
-    for (int f = threadIdx.x * 4; f < SLOT_FLOATS; f += kThreads * 4) {
-      const int wv = f / (kRowsPerWave * D);
-      const int row = (f / D) % kRowsPerWave;
-      const int d = f % D;
-      const int q_loc = q_lo + (wv >> p.hpw_log2) * kRowsPerWave + row;
-      if (q_loc >= Lq) continue;
-      const int h = hg * hpw + (wv & (hpw - 1));
-      f32x4_t acc = *(const f32x4_t*)(base + f);
-      for (int k = 1; k < nk; ++k) {
-        const f32x4_t x = *(const f32x4_t*)(base + k * chunk_stride + f);
+    for (int f4 = threadIdx.x; f4 < rows * (D / 4); f4 += kThreads) {
+      const int row = f4 / (D / 4), d = (f4 % (D / 4)) * 4;
+      const float* src = base + (size_t)row * D + d;
+      f32x4_t acc = *(const f32x4_t*)src;
+      int k = 1;
+      for (; k + 4 <= nk; k += 4) {
+        f32x4_t x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += x[e];
+        for (int u = 0; u < 4; ++u) x[u] = *(const f32x4_t*)(src + (k + u) * chunk_stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] += x[u][c];
+      }
+      for (; k < nk; ++k) {
+        const f32x4_t x = *(const f32x4_t*)(src + k * chunk_stride);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] += x[c];
       }
       T y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = (T)(acc[e] * p.out_mul);
-      *(u32x2_t*)((T*)p.out + ((size_t)(q_tok0 + q_loc) * p.Hq + h) * D + d) = *(const u32x2_t*)y;
+      for (int c = 0; c < 4; ++c) y[c] = (T)(acc[c] * p.out_mul);
+      *(u32x2_t*)((T*)p.out + ((size_t)(q_tok0 + row0 + row) * p.Hq + h) * D + d) = *(const u32x2_t*)y;
     }
   }
 }
@@ -2401,7 +2416,7 @@ hipError_t launch_run(const FwdArgs& a) {
   if (err != hipSuccess || p.split_slots == 0) return err;
   KernelFn red = pick_reduce(a.dtype, a.head_dim, a.paged);
   if (!red) return hipErrorInvalidValue;
-  const long long rupper = (long long)(p.split_slots / 2) * p.n_hg;
+  const long long rupper = (long long)(p.split_slots / 2) * p.n_hg * kWaves;
   const long long rcap = (long long)num_cus() * 4;
   hipLaunchKernelGGL(red, dim3((int)(rupper < rcap ? rupper : rcap)), dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
