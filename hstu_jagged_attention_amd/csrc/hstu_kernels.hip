@@ -388,19 +388,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int causa
   __syncthreads();
   const int T = chunk_tiles;
   auto n_chunks = [&](int c) { return c > T ? min((c + T - 1) / T, 255) : 1; };
-  // Cost of chunk k of nk of an item of cost c.
+  // Cost of chunk k of nk of an item of cost c: c / nk or c / nk + 1, the
+  // latter for c % nk of the chunks.
   auto chunk_cost = [&](int c, int k, int nk) { return nk == 1 ? c : (k + 1) * c / nk - k * c / nk; };
   if (T != INT_MAX) {  // uniform; without splits the histogram and count above already hold
+    // Chunks per cost, from the items per cost (thread tid holds cost
+    // tid): every item of cost c splits alike, so each bin adds its items'
+    // chunks to at most two bins (one atomic each instead of one per chunk,
+    // which serialised on the few popular chunk costs).
+    const int h = hist[tid];
+    __syncthreads();
     if (tid == 0) count = 0;
     hist[tid] = 0;
     __syncthreads();
-    for (int base = 0; base < n_items; base += kPlanThreads) {
-      const int idx = base + tid;
-      const int c = idx < n_items ? cost_of(idx) : -1;
-      const int nk = c < 0 ? 0 : n_chunks(c);
-      for (int k = 0; k < nk; ++k) atomicAdd(&hist[chunk_cost(c, k, nk)], 1);
-      wave_fetch_add(&count, nk);
+    const int nk = h > 0 ? n_chunks(tid) : 0;
+    if (nk > 0) {
+      const int q = tid / nk, r = tid - q * nk;
+      if (nk - r > 0) atomicAdd(&hist[q], h * (nk - r));
+      if (r > 0) atomicAdd(&hist[q + 1], h * r);
     }
+    wave_fetch_add(&count, h * nk);
     __syncthreads();
   }
   // Exclusive scan over bins in descending cost: start[c] = sum of hist[c']
@@ -437,8 +444,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int causa
       p.split_items[4 * split_at + 2] = s.q_tok0;
       p.split_items[4 * split_at + 3] = s.Lq;
     }
-    for (int k = 0; k < nk; ++k) {
-      const int pos = atomicAdd(&hist[chunk_cost(c, k, nk)], 1);
+    // The item's chunks of cost q take consecutive positions in that bin,
+    // and those of cost q + 1 in the next: two atomics per item.
+    const int q = c / nk, r = c - q * nk;
+    const int pos_lo = nk - r > 0 ? atomicAdd(&hist[q], nk - r) : 0;
+    const int pos_hi = r > 0 ? atomicAdd(&hist[q + 1], r) : 0;
+    for (int k = 0, n_lo = 0, n_hi = 0; k < nk; ++k) {
+      const int pos = chunk_cost(c, k, nk) == q ? pos_lo + n_lo++ : pos_hi + n_hi++;
       p.items[2 * pos] = (b << 16) | qt;
       p.items[2 * pos + 1] = (k << 24) | (nk << 16) | slot;
     }
