@@ -365,6 +365,32 @@ def test_paged_dtypes(dev, dtype, D):
     assert_parity(got, oracle_paged(pc), dtype, f"paged {dtype} D={D}")
 
 
+# Key-split calls whose items split into about eight chunks each (the
+# reduction's loads of four chunks at a time and their remainder; the
+# planner's per-cost chunk positions), with query counts on both sides of
+# every 32-row block of an item.
+SPLIT_ROWS = [1, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 200]
+
+
+def test_key_split_many_chunks_row_blocks_jagged(dev):
+    lk = [4000 + 37 * i for i in range(len(SPLIT_ROWS))]
+    c = wl.jagged_case(61, lk, 4, 4, 128, "bf16", num_targets=SPLIT_ROWS, target_group_size=1,
+                       q_lengths=SPLIT_ROWS, max_seq_len=4500, name="split_many_jagged")
+    say(c.name, "batch", c.batch)
+    got = run_jagged(c, dev)
+    assert_parity(got, oracle_jagged(c), "bf16", c.name)
+
+
+@pytest.mark.parametrize("Hq,Hk", [(4, 4), (8, 4)])
+def test_key_split_many_chunks_row_blocks_paged(dev, Hq, Hk):
+    newl = [1, 31, 32, 33, 63, 64, 65, 100]
+    hist = [3900 + 53 * i for i in range(len(newl))]
+    pc = wl.paged_case(62 + Hq, hist, newl, Hq, Hk, 128, "f16", page_size=64, target_group_size=1)
+    say("split_many_paged", Hq, Hk)
+    got = run_paged(pc, dev)
+    assert_parity(got, oracle_paged(pc), "f16", f"split_many_paged {Hq}/{Hk}")
+
+
 def test_paged_equals_gathered_jagged_on_gpu(dev):
     pc = wl.paged_case(41, [130, 64, 5], [9, 3, 12], 4, 4, 128, "bf16", page_size=64, num_context=(0, 3),
                        target_group_size=1)
