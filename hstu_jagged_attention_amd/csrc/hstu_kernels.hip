@@ -1691,38 +1691,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
 
       // Epilogue: P = min(silu(alpha s), 448), cast to E4M3, packed as the
-      // B operand of O^T (byte order in the comment above the kernel).
+      // B operand of O^T (byte order in the comment above the kernel). Full
+      // tiles skip the visibility bit-select (two straight-line copies).
       uint32_t vis[NJB];
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const int jbase = j0 + jb * 32 + 4 * half;
-        const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
-        vis[jb] = full ? 0xffffffffu : (low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg)));
-        if (windowed && !full) vis[jb] &= ~low_bits(i - p.win + 1 - jbase);
-      }
-      auto pval = [&](int jb, int r) -> float {
-        float sv = sacc[jb][r];
-        // Masked keys get s = +0 (bitwise AND with the visibility bit), hence p = 0 exactly.
-        const int off = 8 * (r / 4) + (r % 4);
-        const int keep = (int)(vis[jb] << (31 - off)) >> 31;
-        sv = __builtin_bit_cast(float, __builtin_bit_cast(int, sv) & keep);
-        const float a = sv * p.alpha;
-        const float e = __builtin_amdgcn_exp2f(a * -kLog2e);
-        const float pv = a * __builtin_amdgcn_rcpf(1.f + e);
-        return __builtin_fminf(pv, 448.f);
-      };
-      // Word 2 q + w holds bytes 8 q + 4 w .. + 3, i.e. i2 = 2 w (low half) and
-      // i2 = 2 w + 1 (high half) of the pairs (i, i + 1) = (2 i2, 2 i2 + 1).
       i32x8_t pb = {};
+      auto epilogue = [&](auto masked) {
+        if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int wh = 0; wh < 2; ++wh) {
-          const int jb = q >> 1, r_lo = 4 * (2 * wh) + 2 * (q & 1), r_hi = 4 * (2 * wh + 1) + 2 * (q & 1);
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(pval(jb, r_lo), pval(jb, r_lo + 1), 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(pval(jb, r_hi), pval(jb, r_hi + 1), word, true);
-          pb[2 * q + wh] = word;
+          for (int jb = 0; jb < NJB; ++jb) {
+            const int jbase = j0 + jb * 32 + 4 * half;
+            const int lo_end = a_i - jbase + 1, hi_beg = b_i == INT_MAX ? 32 : b_i - jbase, hi_end = i - jbase + 1;
+            vis[jb] = low_bits(lo_end) | (low_bits(hi_end) & ~low_bits(hi_beg));
+            if (windowed) vis[jb] &= ~low_bits(i - p.win + 1 - jbase);
+          }
         }
+        auto pval = [&](int jb, int r) -> float {
+          float sv = sacc[jb][r];
+          if constexpr (decltype(masked)::value) {
+            // Masked keys get s = +0 (bitwise AND with the visibility bit), hence p = 0 exactly.
+            const int off = 8 * (r / 4) + (r % 4);
+            const int keep = (int)(vis[jb] << (31 - off)) >> 31;
+            sv = __builtin_bit_cast(float, __builtin_bit_cast(int, sv) & keep);
+          }
+          const float a = sv * p.alpha;
+          const float e = __builtin_amdgcn_exp2f(a * -kLog2e);
+          const float pv = a * __builtin_amdgcn_rcpf(1.f + e);
+          return __builtin_fminf(pv, 448.f);
+        };
+        // Word 2 q + w holds bytes 8 q + 4 w .. + 3, i.e. i2 = 2 w (low half)
+        // and i2 = 2 w + 1 (high half) of the pairs (i, i + 1) = (2 i2, 2 i2 + 1).
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int wh = 0; wh < 2; ++wh) {
+            const int jb = q >> 1, r_lo = 4 * (2 * wh) + 2 * (q & 1), r_hi = 4 * (2 * wh + 1) + 2 * (q & 1);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(pval(jb, r_lo), pval(jb, r_lo + 1), 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(pval(jb, r_hi), pval(jb, r_hi + 1), word, true);
+            pb[2 * q + wh] = word;
+          }
+      };
+      if (full)
+        epilogue(std::false_type{});
+      else
+        epilogue(std::true_type{});
 
       // O^T += V^T P^T: four transposing reads per 32-feature block.
 #pragma unroll
