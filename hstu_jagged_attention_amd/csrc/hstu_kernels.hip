@@ -349,14 +349,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int causa
     return min(tile_count(tile_range(s, i_lo, i_hi, p.g, p.win, causal != 0, BN)), kMaxBins - 1);
   };
   auto cost_of = [&](int idx) -> int { return idx < kCostCache ? (int)cost_cache[idx] : compute_cost(idx); };
-  for (int base = 0; base < n_items; base += kPlanThreads) {  // uniform trip count: wave ops below
+  // The planner runs on one CU, so its passes over the items are
+  // instruction-bound: the totals are summed per thread and added once.
+  int my_cost = 0, my_count = 0;
+  for (int base = 0; base < n_items; base += kPlanThreads) {
     const int idx = base + tid;
     const int c = idx < n_items ? compute_cost(idx) : -1;
     if (idx < kCostCache && idx < n_items) cost_cache[idx] = (short)c;
-    if (c >= 0) atomicAdd(&hist[c], 1);
-    wave_fetch_add(&total_cost, max(c, 0));
-    wave_fetch_add(&count, c >= 0 ? 1 : 0);
+    if (c >= 0) {
+      atomicAdd(&hist[c], 1);
+      my_cost += c;
+      ++my_count;
+    }
   }
+  wave_fetch_add(&total_cost, my_cost);
+  wave_fetch_add(&count, my_count);
   __syncthreads();
   // Chunk size from the cost histogram (no further pass over the items):
   // candidates t0, 2 t0, 4 t0, ... in turn, one histogram bin per thread;
@@ -429,8 +436,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int causa
     const int c = idx < n_items ? cost_of(idx) : -1;
     const int nk = c < 0 ? 0 : n_chunks(c);
     const int split_nk = nk > 1 ? nk : 0;
-    const int slot_at = wave_fetch_add(&slot_alloc, split_nk);
-    const int split_at = wave_fetch_add(&n_split, split_nk ? 1 : 0);
+    int slot_at = 0, split_at = 0;
+    if (T != INT_MAX) {  // uniform: only calls that split need slots
+      slot_at = wave_fetch_add(&slot_alloc, split_nk);
+      split_at = wave_fetch_add(&n_split, split_nk ? 1 : 0);
+    }
     if (c < 0) continue;
     int b, qt;
     split_idx(idx, b, qt);
