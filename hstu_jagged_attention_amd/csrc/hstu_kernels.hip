@@ -191,7 +191,8 @@ __device__ inline Tiles tile_range(const Seq& s, int i_lo, int i_hi, int g, int 
     a_end = i_hi + 1;
   } else {
     a_end = s.H;
-    b_lo = s.H + ((max(i_lo, s.H) - s.H) / g) * g;
+    const int d = max(i_lo, s.H) - s.H;
+    b_lo = s.H + (g == 1 ? d : (d / g) * g);  // group start of row i_lo (no division for groups of one)
     b_end = i_hi + 1;
   }
   const int w_lo = win > 0 ? max(i_lo - win + 1, 0) : 0;  // first key inside some row's window
@@ -453,6 +454,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(KParams p, int causa
       p.split_items[4 * split_at + 1] = (nk << 16) | slot;
       p.split_items[4 * split_at + 2] = s.q_tok0;
       p.split_items[4 * split_at + 3] = s.Lq;
+    }
+    if (nk == 1) {  // unsplit: one position in its cost's bin, no divisions
+      const int pos = atomicAdd(&hist[c], 1);
+      p.items[2 * pos] = (b << 16) | qt;
+      p.items[2 * pos + 1] = (1 << 16) | slot;
+      continue;
     }
     // The item's chunks of cost q take consecutive positions in that bin,
     // and those of cost q + 1 in the next: two atomics per item.
