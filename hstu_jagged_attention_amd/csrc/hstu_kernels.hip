@@ -94,7 +94,7 @@ struct KParams {
   int32_t* split_items;  // split items: four ints each (see the planner)
   int32_t* n_split;      // number of split items
   int32_t split_slots;   // partial-sum slots available (0: never split)
-  int32_t target_chunks; // chunks the planner aims for (one per two resident workgroups)
+  int32_t target_chunks; // chunks the planner aims for (per resident workgroup: 1/2 paged, 1 jagged)
   int32_t* counter;   // work-queue head
   int32_t* exited;    // workgroups that left the queue (the last one resets both counters)
   int32_t batch;
@@ -222,8 +222,8 @@ __device__ inline int nth_tile(const Tiles& t, int n) {
 // first query, and its query count (at most half as many entries as slots,
 // so the list fits the two ints per slot the workspace reserves).
 // Chunk size: the total work over target_chunks (one chunk per two resident
-// workgroups; at least kMinChunkTiles), doubled until the split items fit
-// the partial-sum slots.
+// workgroups on paged calls, one per workgroup on jagged ones; at least
+// kMinChunkTiles), doubled until the split items fit the partial-sum slots.
 // ------------------------------------------------------------------------
 // Wave-wide inclusive prefix sum (64 lanes) by DPP lane shifts: within each
 // row of 16 lanes by shifts of 1, 2, 4 and 8, then across rows by the
