@@ -91,7 +91,7 @@ enum Phase { kPlan = 1, kRun = 2, kBoth = 3 };
 
 // HSTU_VALIDATE=1 in the environment (read at every call) turns on the
 // debug check of the device-side inputs: a validation kernel writes its
-// verdict into the workspace header, the call waits for the stream
+// result into the workspace header, the call waits for the stream
 // and reads it, and returns HSTU_ERR_INVALID_ARG without launching the
 // forward kernels when the inputs break the rules. Off by default: the
 // library then never synchronises and never reads device memory.
